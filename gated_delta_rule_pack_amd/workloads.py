@@ -1,0 +1,197 @@
+"""Seeded synthetic workloads for chunkwise KDA prefill.
+
+This module only draws inputs; it holds none of the method's arithmetic. Both the
+HIP path (through the C-ABI binding) and the fp64 oracle consume what it returns,
+so the two sides always see identical bits.
+
+Shapes and value distributions follow the workloads described on the pages:
+packed varlen ``[1, T, H, 128]`` bf16 q/k/v, raw (pre-activation) gate per key
+channel and raw beta per token-head (aiter PR 4741, Summary), a paged fp32/fp16/bf16
+state pool ``[slots, H, V, K]`` with a possibly padded ``stride(0)``, int32
+``state_indices`` and bool ``has_initial_state`` (aiter PR 5754, Technical Details),
+and host copies of ``cu_seqlens`` (aiter PR 6912, Changes).
+
+Generation order is fixed: lengths -> q -> k -> v -> raw gate -> raw beta -> state ->
+indices -> flags, all from one CPU ``torch.Generator`` seeded per workload.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Optional
+
+import numpy as np
+import torch
+
+HEAD_DIM = 128
+
+_DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+@dataclass
+class Workload:
+    """One synthetic KDA prefill call, all tensors on the CPU."""
+
+    name: str
+    q: torch.Tensor  # [1, T, H, K] bf16
+    k: torch.Tensor  # [1, T, H, K] bf16
+    v: torch.Tensor  # [1, T, H, V] bf16
+    g_raw: torch.Tensor  # [1, T, H, K] fp32 (or bf16)
+    beta_raw: torch.Tensor  # [1, T, H] fp32 (or bf16)
+    cu_seqlens: torch.Tensor  # [N+1] int32
+    scale: float
+    lower_bound: float
+    state_mode: str  # "none" | "dense" | "paged"
+    state_dtype: str = "f32"
+    initial_state: Optional[torch.Tensor] = None  # dense [N, H, V, K]
+    want_final_state: bool = False  # dense mode: also write final_state
+    state_storage: Optional[torch.Tensor] = None  # paged: flat storage [slots, stride0]
+    state_stride0: int = 0  # paged: elements between slots (>= H*V*K)
+    num_slots: int = 0
+    state_indices: Optional[torch.Tensor] = None  # [N] int32
+    has_initial_state: Optional[torch.Tensor] = None  # [N] bool
+    info: dict = field(default_factory=dict)
+
+    @property
+    def T(self) -> int:
+        return int(self.q.shape[1])
+
+    @property
+    def H(self) -> int:
+        return int(self.q.shape[2])
+
+    @property
+    def N(self) -> int:
+        return int(self.cu_seqlens.numel()) - 1
+
+    def cache_view(self) -> torch.Tensor:
+        """The pool as ``[slots, H, V, K]`` (a strided view of the flat storage)."""
+        assert self.state_storage is not None
+        H = self.H
+        return self.state_storage.as_strided(
+            (self.num_slots, H, HEAD_DIM, HEAD_DIM),
+            (self.state_stride0, HEAD_DIM * HEAD_DIM, HEAD_DIM, 1),
+        )
+
+
+def to_f64(t: torch.Tensor) -> np.ndarray:
+    """Exact upcast of a stored tensor (bf16/fp16/fp32/int) to an fp64 numpy array."""
+    return t.detach().to("cpu").to(torch.float64).numpy()
+
+
+def _randn(gen: torch.Generator, shape, std: float = 1.0) -> torch.Tensor:
+    return torch.randn(shape, generator=gen, dtype=torch.float32) * std
+
+
+def _lengths_to_cu(lengths) -> torch.Tensor:
+    cu = np.zeros(len(lengths) + 1, dtype=np.int64)
+    cu[1:] = np.cumsum(np.asarray(lengths, dtype=np.int64))
+    return torch.from_numpy(cu.astype(np.int32))
+
+
+def make_workload(
+    name: str,
+    lengths,
+    H: int,
+    *,
+    seed: int,
+    state_mode: str = "none",
+    state_dtype: str = "f32",
+    num_slots: int = 0,
+    stride_pad: int = 0,
+    has_initial: str = "all",  # "all" | "none" | "bernoulli"
+    gate_shift: float = 0.0,
+    lower_bound: float = -5.0,
+    beta_dtype: str = "f32",
+    gate_dtype: str = "f32",
+    state_std: float = 0.1,
+    poison: bool = True,
+    want_final_state: bool = True,
+    lengths_from_seed: Optional[tuple] = None,
+) -> Workload:
+    """Draw one workload.
+
+    ``lengths`` is a list of per-sequence token counts, or None when
+    ``lengths_from_seed=(N, lo, hi, n_zero)`` asks for N lengths uniform in [lo, hi]
+    with ``n_zero`` positions (a seeded permutation) forced to 0.
+    """
+    gen = torch.Generator("cpu").manual_seed(seed)
+    if lengths is None:
+        n, lo, hi, n_zero = lengths_from_seed
+        lens = torch.randint(lo, hi + 1, (n,), generator=gen).tolist()
+        zero_pos = torch.randperm(n, generator=gen)[:n_zero].tolist()
+        for p in zero_pos:
+            lens[p] = 0
+        lengths = lens
+    lengths = [int(x) for x in lengths]
+    cu = _lengths_to_cu(lengths)
+    T = int(cu[-1])
+    N = len(lengths)
+    K = V = HEAD_DIM
+
+    q = _randn(gen, (1, T, H, K)).to(torch.bfloat16)
+    k = _randn(gen, (1, T, H, K)).to(torch.bfloat16)
+    v = _randn(gen, (1, T, H, V)).to(torch.bfloat16)
+    g_raw = (_randn(gen, (1, T, H, K)) + gate_shift).to(_DTYPES[gate_dtype])
+    beta_raw = _randn(gen, (1, T, H)).to(_DTYPES[beta_dtype])
+
+    wl = Workload(
+        name=name, q=q, k=k, v=v, g_raw=g_raw, beta_raw=beta_raw, cu_seqlens=cu,
+        scale=1.0 / float(np.sqrt(K)), lower_bound=float(lower_bound), state_mode=state_mode,
+        state_dtype=state_dtype, info={"lengths": lengths, "seed": seed},
+    )
+    sdt = _DTYPES[state_dtype]
+    if state_mode == "dense":
+        wl.initial_state = _randn(gen, (N, H, V, K), state_std).to(sdt)
+        wl.want_final_state = want_final_state
+    elif state_mode == "paged":
+        assert num_slots >= N
+        plane = H * V * K
+        stride0 = plane + int(stride_pad)
+        storage = _randn(gen, (num_slots, stride0), state_std)
+        if stride_pad and poison:
+            storage[:, plane:] = float("nan")  # stride padding: must never be touched
+        storage = storage.to(sdt)
+        idx = torch.randperm(num_slots, generator=gen)[:N].to(torch.int32)
+        if has_initial == "all":
+            flags = torch.ones(N, dtype=torch.bool)
+        elif has_initial == "none":
+            flags = torch.zeros(N, dtype=torch.bool)
+        else:
+            flags = torch.rand(N, generator=gen) < 0.5
+        if poison:
+            # A slot whose has_initial_state is false must not be read: poison it.
+            for n in range(N):
+                if not bool(flags[n]):
+                    storage[int(idx[n]), :plane] = float("nan")
+        wl.state_storage = storage
+        wl.state_stride0 = stride0
+        wl.num_slots = num_slots
+        wl.state_indices = idx
+        wl.has_initial_state = flags
+    elif state_mode != "none":
+        raise ValueError(state_mode)
+    return wl
+
+
+# The five workloads of the benchmark plan, seeds 1000 + i.
+def config(i: int, **overrides) -> Workload:
+    """Workload ``i`` (1-based) of the five standard shapes; ``overrides`` adjust it."""
+    if i == 1:
+        kw = dict(name="cfg1_T256_H1_dense", lengths=[256], H=1, seed=1001, state_mode="dense")
+    elif i == 2:
+        kw = dict(name="cfg2_1x4096_H12_paged", lengths=[4096], H=12, seed=1002,
+                  state_mode="paged", num_slots=64)
+    elif i == 3:
+        kw = dict(name="cfg3_1x16384_H12_paged_pad", lengths=[16384], H=12, seed=1003,
+                  state_mode="paged", num_slots=64, stride_pad=4096)
+    elif i == 4:
+        kw = dict(name="cfg4_varlen128_H12_paged", lengths=None, H=12, seed=1004,
+                  state_mode="paged", num_slots=256, has_initial="bernoulli",
+                  lengths_from_seed=(128, 0, 2048, 4))
+    elif i == 5:
+        kw = dict(name="cfg5_256xT1_H12_paged_bf16", lengths=[1] * 256, H=12, seed=1005,
+                  state_mode="paged", state_dtype="bf16", num_slots=512)
+    else:
+        raise ValueError(i)
+    kw.update(overrides)
+    return make_workload(**kw)
