@@ -1,0 +1,572 @@
+// Host side of the KDA prefill library: argument validation, chunk metadata, the
+// content-keyed metadata cache with asynchronous uploads from pinned memory, and the
+// launch sequence (prep, then scan) on the caller's stream.
+//
+// Metadata handling follows aiter PR 6912 (Changes): tables are built from host bounds
+// when the caller has them (no read-back), otherwise the bounds are read back once;
+// chunks are numbered by their sequence's position in cu_seqlens (an empty sequence
+// contributes none); the tables share one int32 buffer whose blocks start 16-byte
+// aligned and go up with one non-blocking copy from pinned memory; the buffer is cached
+// on the bounds' contents; a hit from another stream waits on the uploading stream; a
+// miss while the stream is being captured is an error; a buffer a captured stream has
+// used is kept for the context's lifetime.
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <unordered_map>
+#include <vector>
+
+#include "kda.h"
+#include "kda_internal.h"
+
+using kda::kChunk;
+using kda::kHead;
+
+namespace {
+
+// ------------------------------------------------------------------ real HIP runtime
+int rt_h2d(void*, void* dst, const void* src, size_t n, void* s) {
+  return (int)hipMemcpyAsync(dst, src, n, hipMemcpyHostToDevice, (hipStream_t)s);
+}
+int rt_d2h(void*, void* dst, const void* src, size_t n, void* s) {
+  return (int)hipMemcpyAsync(dst, src, n, hipMemcpyDeviceToHost, (hipStream_t)s);
+}
+int rt_sync(void*, void* s) { return (int)hipStreamSynchronize((hipStream_t)s); }
+int rt_capturing(void*, void* s, int* cap) {
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  hipError_t e = hipStreamIsCapturing((hipStream_t)s, &st);
+  *cap = (st == hipStreamCaptureStatusActive) ? 1 : 0;
+  return (int)e;
+}
+int rt_ev_create(void*, void** ev) {
+  return (int)hipEventCreateWithFlags(reinterpret_cast<hipEvent_t*>(ev), hipEventDisableTiming);
+}
+int rt_ev_destroy(void*, void* ev) { return (int)hipEventDestroy((hipEvent_t)ev); }
+int rt_ev_record(void*, void* ev, void* s) { return (int)hipEventRecord((hipEvent_t)ev, (hipStream_t)s); }
+int rt_ev_query(void*, void* ev) {
+  hipError_t e = hipEventQuery((hipEvent_t)ev);
+  if (e == hipSuccess) return 0;
+  if (e == hipErrorNotReady) return 1;
+  return -1;
+}
+int rt_ev_sync(void*, void* ev) { return (int)hipEventSynchronize((hipEvent_t)ev); }
+int rt_wait(void*, void* s, void* ev) { return (int)hipStreamWaitEvent((hipStream_t)s, (hipEvent_t)ev, 0); }
+int rt_host_alloc(void*, void** p, size_t n) { return (int)hipHostMalloc(p, n, hipHostMallocDefault); }
+int rt_host_free(void*, void* p) { return (int)hipHostFree(p); }
+int rt_dev_alloc(void*, void** p, size_t n) { return (int)hipMalloc(p, n); }
+int rt_dev_free(void*, void* p) { return (int)hipFree(p); }
+int rt_launch(void*, int kernel, const void* plan, void* s) {
+  const kda::Plan& p = *reinterpret_cast<const kda::Plan*>(plan);
+  return kernel == 0 ? kda::launch_prep(p, s) : kda::launch_scan(p, s);
+}
+
+const kda_runtime kHipRuntime = {nullptr,    rt_h2d,        rt_d2h,         rt_sync,     rt_capturing,
+                                 rt_ev_create, rt_ev_destroy, rt_ev_record, rt_ev_query, rt_ev_sync,
+                                 rt_wait,    rt_host_alloc, rt_host_free,   rt_dev_alloc, rt_dev_free,
+                                 rt_launch};
+
+// ------------------------------------------------------------------ metadata
+inline size_t align4(size_t n) { return (n + 3) & ~size_t(3); }  // int32 count -> 16-byte blocks
+
+struct Meta {
+  int N = 0;
+  int64_t n_chunks = 0;
+  size_t off_cu = 0, off_co = 0, off_table = 0, words = 0;  // in int32 units
+};
+
+// Layout of the single int32 metadata buffer for N sequences and n_chunks chunks.
+Meta meta_layout(int N, int64_t n_chunks) {
+  Meta m;
+  m.N = N;
+  m.n_chunks = n_chunks;
+  m.off_cu = 0;
+  m.off_co = align4(N + 1);
+  m.off_table = m.off_co + align4(N + 1);
+  m.words = m.off_table + align4((size_t)2 * n_chunks);
+  return m;
+}
+
+int64_t count_chunks(const int32_t* cu, int N) {
+  int64_t n = 0;
+  for (int i = 0; i < N; ++i) n += (cu[i + 1] - cu[i] + kChunk - 1) / kChunk;
+  return n;
+}
+
+void build_meta(const int32_t* cu, const Meta& m, int32_t* buf) {
+  std::memset(buf, 0, m.words * sizeof(int32_t));
+  int32_t* co = buf + m.off_co;
+  int32_t* table = buf + m.off_table;
+  int64_t c = 0;
+  for (int i = 0; i <= m.N; ++i) buf[m.off_cu + i] = cu[i];
+  for (int i = 0; i < m.N; ++i) {
+    co[i] = (int32_t)c;
+    const int nc = (cu[i + 1] - cu[i] + kChunk - 1) / kChunk;
+    for (int j = 0; j < nc; ++j, ++c) {
+      table[2 * c] = i;
+      table[2 * c + 1] = j;
+    }
+  }
+  co[m.N] = (int32_t)c;
+}
+
+uint64_t hash_bounds(const int32_t* cu, int N) {
+  uint64_t h = 1469598103934665603ull ^ (uint64_t)N;
+  for (int i = 0; i <= N; ++i) {
+    h ^= (uint32_t)cu[i];
+    h *= 1099511628211ull;
+  }
+  return h;
+}
+
+bool bounds_ok(const int32_t* cu, int N, int T) {
+  if (cu[0] != 0 || cu[N] != T) return false;
+  for (int i = 0; i < N; ++i)
+    if (cu[i + 1] < cu[i]) return false;
+  return true;
+}
+
+int32_t dv_split_for(int32_t N, int32_t H, int32_t cus) {
+  const int64_t units = (int64_t)N * H;
+  for (int s : {8, 4, 2})
+    if (units * s <= 2 * (int64_t)cus) return s;
+  return 2;
+}
+
+int32_t ref_block_for(float lb) {
+  const float a = std::fabs(lb);
+  for (int s : {16, 8, 4, 2})
+    if ((float)(s - 1) * a <= 80.0f) return s;
+  return 1;
+}
+
+bool ranges_overlap(const void* a, size_t an, const void* b, size_t bn) {
+  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return an && bn && a0 < b0 + bn && b0 < a0 + an;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+}  // namespace
+
+// ------------------------------------------------------------------ context
+struct CacheEntry {
+  std::vector<int32_t> bounds;  // key: the full bounds array
+  uint64_t hash = 0;
+  void* dev = nullptr;          // device metadata buffer
+  size_t bytes = 0;
+  Meta meta;
+  void* upload_event = nullptr;
+  void* upload_stream = nullptr;
+  std::vector<std::pair<void*, void*>> uses;  // (stream, event recorded after the last use)
+  bool retained = false;                      // used under graph capture: never freed early
+  uint64_t tick = 0;
+};
+
+struct Staging {
+  void* host = nullptr;
+  size_t bytes = 0;
+  void* event = nullptr;  // recorded after the copy out of this buffer
+  bool used = false;
+};
+
+struct Graveyard {
+  void* dev;
+  std::vector<std::pair<void*, void*>> uses;
+};
+
+struct kda_ctx {
+  kda_runtime rt{};
+  int cu_count = 0;
+  std::vector<CacheEntry*> cache;
+  std::vector<Graveyard> graveyard;
+  std::vector<Staging> ring;
+  size_t ring_next = 0;
+  void* bounds_host = nullptr;  // pinned landing area for bounds read-backs
+  size_t bounds_host_bytes = 0;
+  uint64_t tick = 0;
+  kda_stats stats{};
+};
+
+namespace {
+
+constexpr size_t kCacheCap = 64;
+constexpr size_t kRingSlots = 32;
+
+kda_status hip_fail() { return KDA_ERR_HIP; }
+
+void release_events(kda_ctx* ctx, std::vector<std::pair<void*, void*>>& uses) {
+  for (auto& u : uses) ctx->rt.event_destroy(ctx->rt.user, u.second);
+  uses.clear();
+}
+
+bool uses_done(kda_ctx* ctx, const std::vector<std::pair<void*, void*>>& uses) {
+  for (auto& u : uses)
+    if (ctx->rt.event_query(ctx->rt.user, u.second) != 0) return false;
+  return true;
+}
+
+// Free evicted buffers whose last uses have completed (never waits).
+void sweep_graveyard(kda_ctx* ctx) {
+  auto& gy = ctx->graveyard;
+  for (size_t i = 0; i < gy.size();) {
+    if (uses_done(ctx, gy[i].uses)) {
+      release_events(ctx, gy[i].uses);
+      ctx->rt.device_free(ctx->rt.user, gy[i].dev);
+      gy[i] = gy.back();
+      gy.pop_back();
+    } else {
+      ++i;
+    }
+  }
+}
+
+void evict_one(kda_ctx* ctx) {
+  // Least recently used entry that is not retained.
+  int victim = -1;
+  for (size_t i = 0; i < ctx->cache.size(); ++i) {
+    if (ctx->cache[i]->retained) continue;
+    if (victim < 0 || ctx->cache[i]->tick < ctx->cache[victim]->tick) victim = (int)i;
+  }
+  if (victim < 0) return;
+  CacheEntry* e = ctx->cache[victim];
+  Graveyard g{e->dev, std::move(e->uses)};
+  if (e->upload_event) g.uses.push_back({e->upload_stream, e->upload_event});
+  ctx->graveyard.push_back(std::move(g));
+  ctx->cache.erase(ctx->cache.begin() + victim);
+  delete e;
+}
+
+kda_status record_use(kda_ctx* ctx, CacheEntry* e, void* stream) {
+  for (auto& u : e->uses)
+    if (u.first == stream) return ctx->rt.event_record(ctx->rt.user, u.second, stream) ? hip_fail() : KDA_OK;
+  void* ev = nullptr;
+  if (ctx->rt.event_create(ctx->rt.user, &ev)) return hip_fail();
+  if (ctx->rt.event_record(ctx->rt.user, ev, stream)) return hip_fail();
+  e->uses.push_back({stream, ev});
+  return KDA_OK;
+}
+
+// Find or upload the metadata for these bounds.
+kda_status get_meta(kda_ctx* ctx, const int32_t* cu, int N, void* stream, CacheEntry** out) {
+  int capturing = 0;
+  if (ctx->rt.stream_is_capturing(ctx->rt.user, stream, &capturing)) return hip_fail();
+  const uint64_t hsh = hash_bounds(cu, N);
+  for (CacheEntry* e : ctx->cache) {
+    if (e->hash == hsh && (int)e->bounds.size() == N + 1 &&
+        std::memcmp(e->bounds.data(), cu, (N + 1) * sizeof(int32_t)) == 0) {
+      if (e->upload_stream != stream && e->upload_event) {
+        if (ctx->rt.stream_wait_event(ctx->rt.user, stream, e->upload_event)) return hip_fail();
+      }
+      if (capturing) e->retained = true;
+      e->tick = ++ctx->tick;
+      ctx->stats.cache_hits++;
+      *out = e;
+      return KDA_OK;
+    }
+  }
+  if (capturing) return KDA_ERR_CAPTURE_MISS;
+
+  sweep_graveyard(ctx);
+  while (ctx->cache.size() >= kCacheCap) {
+    const size_t before = ctx->cache.size();
+    evict_one(ctx);
+    if (ctx->cache.size() == before) break;  // everything retained
+  }
+  const Meta m = meta_layout(N, count_chunks(cu, N));
+  const size_t bytes = m.words * sizeof(int32_t);
+
+  // Pinned staging slot: reuse only once its previous copy has completed.
+  Staging& st = ctx->ring[ctx->ring_next];
+  ctx->ring_next = (ctx->ring_next + 1) % ctx->ring.size();
+  if (st.used && ctx->rt.event_query(ctx->rt.user, st.event) != 0) {
+    if (ctx->rt.event_synchronize(ctx->rt.user, st.event)) return hip_fail();
+    ctx->stats.blocking_syncs++;
+  }
+  if (st.bytes < bytes) {
+    if (st.host) ctx->rt.host_free_pinned(ctx->rt.user, st.host);
+    st.host = nullptr;
+    st.bytes = 0;
+    const size_t want = std::max<size_t>(bytes, 4096);
+    if (ctx->rt.host_alloc_pinned(ctx->rt.user, &st.host, want)) return hip_fail();
+    st.bytes = want;
+  }
+  build_meta(cu, m, reinterpret_cast<int32_t*>(st.host));
+
+  CacheEntry* e = new (std::nothrow) CacheEntry();
+  if (!e) return KDA_ERR_HIP;
+  e->bounds.assign(cu, cu + N + 1);
+  e->hash = hsh;
+  e->meta = m;
+  e->bytes = bytes;
+  if (ctx->rt.device_alloc(ctx->rt.user, &e->dev, bytes)) {
+    delete e;
+    return hip_fail();
+  }
+  if (ctx->rt.event_create(ctx->rt.user, &e->upload_event) ||
+      ctx->rt.memcpy_h2d_async(ctx->rt.user, e->dev, st.host, bytes, stream) ||
+      ctx->rt.event_record(ctx->rt.user, e->upload_event, stream)) {
+    ctx->rt.device_free(ctx->rt.user, e->dev);
+    delete e;
+    return hip_fail();
+  }
+  e->upload_stream = stream;
+  if (!st.event && ctx->rt.event_create(ctx->rt.user, &st.event)) return hip_fail();
+  if (ctx->rt.event_record(ctx->rt.user, st.event, stream)) return hip_fail();
+  st.used = true;
+  e->tick = ++ctx->tick;
+  ctx->cache.push_back(e);
+  ctx->stats.cache_misses++;
+  ctx->stats.h2d_uploads++;
+  *out = e;
+  return KDA_OK;
+}
+
+size_t elem_bytes(kda_dtype d) { return d == KDA_F32 ? 4 : 2; }
+
+}  // namespace
+
+// ================================================================== public API
+extern "C" {
+
+const char* kda_status_str(kda_status s) {
+  switch (s) {
+    case KDA_OK: return "ok";
+    case KDA_ERR_INVALID_ARG: return "invalid argument";
+    case KDA_ERR_UNSUPPORTED: return "unsupported shape, dtype or device";
+    case KDA_ERR_STATE_MODE: return "conflicting state arguments (dense vs paged)";
+    case KDA_ERR_STRIDE: return "state_cache_stride0 smaller than one H*V*K plane";
+    case KDA_ERR_ALIAS: return "out overlaps v";
+    case KDA_ERR_WORKSPACE: return "workspace missing or too small";
+    case KDA_ERR_CAPTURE_MISS: return "metadata cache miss during stream capture";
+    case KDA_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+int32_t kda_dv_split(int32_t n_seqs, int32_t H, int32_t cu_count) { return dv_split_for(n_seqs, H, cu_count); }
+
+int32_t kda_ref_block(float lower_bound) { return ref_block_for(lower_bound); }
+
+kda_status kda_chunk_fwd_validate(const kda_fwd_args* a) {
+  if (!a) return KDA_ERR_INVALID_ARG;
+  if (a->N < 1 || a->T < 0 || a->H < 1) return KDA_ERR_INVALID_ARG;
+  if (a->K != kHead || a->V != kHead) return KDA_ERR_UNSUPPORTED;
+  if (!std::isfinite(a->scale) || !std::isfinite(a->lower_bound)) return KDA_ERR_INVALID_ARG;
+  if (a->lower_bound > 0.f) return KDA_ERR_UNSUPPORTED;
+  if (a->g_dtype != KDA_F32 && a->g_dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+  if (a->beta_dtype != KDA_F32 && a->beta_dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+  if (a->state_dtype != KDA_F32 && a->state_dtype != KDA_F16 && a->state_dtype != KDA_BF16)
+    return KDA_ERR_UNSUPPORTED;
+  if (!a->cu_seqlens) return KDA_ERR_INVALID_ARG;
+  if ((int64_t)a->T * a->H > (int64_t)INT32_MAX / kHead) return KDA_ERR_UNSUPPORTED;
+  if (a->T > 0) {
+    if (!a->q || !a->k || !a->v || !a->g_raw || !a->beta_raw || !a->out) return KDA_ERR_INVALID_ARG;
+    // 16-byte vector accesses on every token tensor.
+    if (!aligned(a->q, 16) || !aligned(a->k, 16) || !aligned(a->v, 16) || !aligned(a->g_raw, 16) ||
+        !aligned(a->out, 16) || !aligned(a->beta_raw, elem_bytes(a->beta_dtype)))
+      return KDA_ERR_INVALID_ARG;
+  }
+  const bool dense = a->initial_state || a->final_state;
+  const bool paged = a->state_cache != nullptr;
+  if (dense && paged) return KDA_ERR_STATE_MODE;
+  const size_t plane = (size_t)a->H * kHead * kHead;
+  const size_t sz = elem_bytes(a->state_dtype);
+  if (paged) {
+    if (!a->state_indices || !a->has_initial_state || a->num_slots < 1) return KDA_ERR_INVALID_ARG;
+    if (a->state_cache_stride0 < (int64_t)plane) return KDA_ERR_STRIDE;
+    // Every slot plane must keep the 16/8-byte alignment of the state accesses.
+    if (!aligned(a->state_cache, 16) || ((size_t)a->state_cache_stride0 * sz) % 16 != 0)
+      return KDA_ERR_INVALID_ARG;
+  }
+  if (dense) {
+    if ((a->initial_state && !aligned(a->initial_state, 16)) || (a->final_state && !aligned(a->final_state, 16)))
+      return KDA_ERR_INVALID_ARG;
+  }
+  if (a->T > 0) {
+    const size_t tok_bytes = (size_t)a->T * a->H * kHead * 2;
+    if (ranges_overlap(a->out, tok_bytes, a->v, tok_bytes)) return KDA_ERR_ALIAS;
+  }
+  if (a->cu_seqlens_host && !bounds_ok(a->cu_seqlens_host, a->N, a->T)) return KDA_ERR_INVALID_ARG;
+  return KDA_OK;
+}
+
+size_t kda_chunk_fwd_workspace_bytes(const kda_fwd_args* a) {
+  if (kda_chunk_fwd_validate(a) != KDA_OK) return 0;
+  // Chunks over all sequences are at most ceil(T / 32) + N (one partial chunk each).
+  const int64_t max_chunks = ((int64_t)a->T + kChunk - 1) / kChunk + a->N;
+  return (size_t)a->H * (size_t)max_chunks * kda::kRecBytes;
+}
+
+kda_status kda_prepare_chunk_indices(const int32_t* cu_host, int32_t n_seqs, int32_t chunk, int32_t* pairs_out,
+                                     int64_t cap, int64_t* n_out) {
+  if (!cu_host || n_seqs < 0 || chunk < 1 || !n_out) return KDA_ERR_INVALID_ARG;
+  int64_t total = 0;
+  for (int i = 0; i < n_seqs; ++i) {
+    const int32_t len = cu_host[i + 1] - cu_host[i];
+    if (len < 0) return KDA_ERR_INVALID_ARG;
+    total += (len + chunk - 1) / chunk;
+  }
+  *n_out = total;
+  if (total > cap || (total > 0 && !pairs_out)) return KDA_ERR_INVALID_ARG;
+  int64_t c = 0;
+  for (int i = 0; i < n_seqs; ++i) {
+    const int32_t nc = (cu_host[i + 1] - cu_host[i] + chunk - 1) / chunk;
+    for (int32_t j = 0; j < nc; ++j, ++c) {
+      pairs_out[2 * c] = i;
+      pairs_out[2 * c + 1] = j;
+    }
+  }
+  return KDA_OK;
+}
+
+kda_status kda_ctx_create_with_runtime(const kda_runtime* rt, int cu_count, kda_ctx** out) {
+  if (!rt || !out || cu_count < 1) return KDA_ERR_INVALID_ARG;
+  kda_ctx* ctx = new (std::nothrow) kda_ctx();
+  if (!ctx) return KDA_ERR_HIP;
+  ctx->rt = *rt;
+  ctx->cu_count = cu_count;
+  ctx->ring.resize(kRingSlots);
+  *out = ctx;
+  return KDA_OK;
+}
+
+kda_status kda_ctx_create(int device, kda_ctx** out) {
+  if (!out) return KDA_ERR_INVALID_ARG;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, device) != hipSuccess) return KDA_ERR_HIP;
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return KDA_ERR_UNSUPPORTED;
+  return kda_ctx_create_with_runtime(&kHipRuntime, prop.multiProcessorCount, out);
+}
+
+void kda_ctx_destroy(kda_ctx* ctx) {
+  if (!ctx) return;
+  auto& rt = ctx->rt;
+  for (CacheEntry* e : ctx->cache) {
+    if (e->upload_event) rt.event_synchronize(rt.user, e->upload_event);
+    for (auto& u : e->uses) rt.event_synchronize(rt.user, u.second);
+    release_events(ctx, e->uses);
+    if (e->upload_event) rt.event_destroy(rt.user, e->upload_event);
+    rt.device_free(rt.user, e->dev);
+    delete e;
+  }
+  for (auto& g : ctx->graveyard) {
+    for (auto& u : g.uses) rt.event_synchronize(rt.user, u.second);
+    release_events(ctx, g.uses);
+    rt.device_free(rt.user, g.dev);
+  }
+  for (auto& s : ctx->ring) {
+    if (s.event) {
+      rt.event_synchronize(rt.user, s.event);
+      rt.event_destroy(rt.user, s.event);
+    }
+    if (s.host) rt.host_free_pinned(rt.user, s.host);
+  }
+  if (ctx->bounds_host) rt.host_free_pinned(rt.user, ctx->bounds_host);
+  delete ctx;
+}
+
+kda_status kda_get_stats(const kda_ctx* ctx, kda_stats* out) {
+  if (!ctx || !out) return KDA_ERR_INVALID_ARG;
+  *out = ctx->stats;
+  return KDA_OK;
+}
+
+kda_status kda_reset_stats(kda_ctx* ctx) {
+  if (!ctx) return KDA_ERR_INVALID_ARG;
+  ctx->stats = kda_stats{};
+  return KDA_OK;
+}
+
+kda_status kda_chunk_fwd(kda_ctx* ctx, const kda_fwd_args* a, void* ws, size_t ws_bytes, void* stream) {
+  if (!ctx) return KDA_ERR_INVALID_ARG;
+  kda_status st = kda_chunk_fwd_validate(a);
+  if (st != KDA_OK) return st;
+  const size_t need = kda_chunk_fwd_workspace_bytes(a);
+  if (need > 0 && (!ws || ws_bytes < need || !aligned(ws, 256))) return KDA_ERR_WORKSPACE;
+  auto& rt = ctx->rt;
+
+  // Host bounds: given, or read back once (one counted synchronisation).
+  const int32_t* cu = a->cu_seqlens_host;
+  if (!cu) {
+    int capturing = 0;
+    if (rt.stream_is_capturing(rt.user, stream, &capturing)) return hip_fail();
+    if (capturing) return KDA_ERR_CAPTURE_MISS;  // a read-back cannot run under capture
+    const size_t bytes = (size_t)(a->N + 1) * sizeof(int32_t);
+    if (ctx->bounds_host_bytes < bytes) {
+      if (ctx->bounds_host) rt.host_free_pinned(rt.user, ctx->bounds_host);
+      ctx->bounds_host = nullptr;
+      ctx->bounds_host_bytes = 0;
+      if (rt.host_alloc_pinned(rt.user, &ctx->bounds_host, bytes)) return hip_fail();
+      ctx->bounds_host_bytes = bytes;
+    }
+    if (rt.memcpy_d2h_async(rt.user, ctx->bounds_host, a->cu_seqlens, bytes, stream)) return hip_fail();
+    if (rt.stream_synchronize(rt.user, stream)) return hip_fail();
+    ctx->stats.blocking_syncs++;
+    ctx->stats.d2h_reads++;
+    cu = reinterpret_cast<const int32_t*>(ctx->bounds_host);
+    if (!bounds_ok(cu, a->N, a->T)) return KDA_ERR_INVALID_ARG;
+  }
+
+  CacheEntry* e = nullptr;
+  st = get_meta(ctx, cu, a->N, stream, &e);
+  if (st != KDA_OK) return st;
+
+  kda::Plan p{};
+  p.T = a->T;
+  p.N = a->N;
+  p.H = a->H;
+  p.n_chunks = (int)e->meta.n_chunks;
+  p.scale = a->scale;
+  p.lower_bound = a->lower_bound;
+  p.ref_block = ref_block_for(a->lower_bound);
+  p.dv_split = dv_split_for(a->N, a->H, ctx->cu_count);
+  p.q = a->q;
+  p.k = a->k;
+  p.v = a->v;
+  p.g_raw = a->g_raw;
+  p.beta_raw = a->beta_raw;
+  p.g_dtype = a->g_dtype == KDA_F32 ? kda::kF32 : kda::kBF16;
+  p.beta_dtype = a->beta_dtype == KDA_F32 ? kda::kF32 : kda::kBF16;
+  const int32_t* base = reinterpret_cast<const int32_t*>(e->dev);
+  p.d_cu = base + e->meta.off_cu;
+  p.d_co = base + e->meta.off_co;
+  p.d_table = base + e->meta.off_table;
+  p.state_dtype = a->state_dtype == KDA_F32 ? kda::kF32 : (a->state_dtype == KDA_F16 ? kda::kF16 : kda::kBF16);
+  const int64_t plane = (int64_t)a->H * kHead * kHead;
+  if (a->state_cache) {
+    p.state_in = a->state_cache;
+    p.in_mode = kda::kStatePaged;
+    p.state_out = a->state_cache;
+    p.out_mode = kda::kStatePaged;
+    p.stride0 = a->state_cache_stride0;
+  } else {
+    p.state_in = a->initial_state;
+    p.in_mode = a->initial_state ? kda::kStateDense : kda::kStateNone;
+    p.state_out = a->final_state;
+    p.out_mode = a->final_state ? kda::kStateDense : kda::kStateNone;
+    p.stride0 = plane;
+  }
+  p.indices = a->state_indices;
+  p.flags = a->has_initial_state;
+  p.out = a->out;
+  p.ws = ws;
+
+  if (rt.launch(rt.user, 0, &p, stream)) return hip_fail();
+  if (rt.launch(rt.user, 1, &p, stream)) return hip_fail();
+  st = record_use(ctx, e, stream);
+  if (st != KDA_OK) return st;
+  ctx->stats.calls++;
+  ctx->stats.last_dv_split = p.dv_split;
+  ctx->stats.last_ref_block = p.ref_block;
+  ctx->stats.last_n_chunks = e->meta.n_chunks;
+  return KDA_OK;
+}
+
+size_t kda_fwd_args_size(void) { return sizeof(kda_fwd_args); }
+
+}  // extern "C"

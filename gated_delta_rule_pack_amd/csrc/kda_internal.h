@@ -1,0 +1,68 @@
+// Internal declarations shared by the host orchestration and the kernel launchers.
+// Not part of the public ABI (include/kda.h is).
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kda {
+
+constexpr int kChunk = 32;    // tokens per chunk
+constexpr int kHead = 128;    // K = V = 128
+constexpr int kThreadsPrep = 256;
+constexpr int kThreadsScan = 128;
+
+// Per (head, chunk) workspace record written by prep and read by scan. Every tile is
+// stored in the exact per-lane order the scan's MFMA operands use, so the scan issues
+// one contiguous 16-byte load per lane per fragment.
+//   W  : 8 fragments (row tile t in 0..1, key block m in 0..3), bf16
+//   Q  : 8 fragments, same order, bf16 (scale folded in)
+//   K  : 8 fragments (key tile 0..7), bf16
+//   U  : 8 fragments (value slice 0..7 of 16 channels), bf16
+//   P  : 2 fragments (row tile 0..1), bf16 (scale folded in)
+//   E  : 128 fp32, exp(G_C) per key channel
+constexpr size_t kFrag = 64 * 16;  // one fragment: 64 lanes x 16 bytes
+constexpr size_t kRecW = 0;
+constexpr size_t kRecQ = kRecW + 8 * kFrag;
+constexpr size_t kRecK = kRecQ + 8 * kFrag;
+constexpr size_t kRecU = kRecK + 8 * kFrag;
+constexpr size_t kRecP = kRecU + 8 * kFrag;
+constexpr size_t kRecE = kRecP + 2 * kFrag;
+constexpr size_t kRecBytes = kRecE + kHead * 4;  // 35328 = 138 * 256
+static_assert(kRecBytes % 256 == 0, "records stay 256-byte aligned");
+
+enum StateMode : int { kStateNone = 0, kStateDense = 1, kStatePaged = 2 };
+enum DType : int { kF32 = 0, kF16 = 1, kBF16 = 2 };
+
+// Everything one launch needs; filled by the host orchestration.
+struct Plan {
+  int T, N, H, n_chunks;
+  float scale, lower_bound;
+  int ref_block;  // reference-row block of the bounded decay construction
+  int dv_split;   // value-channel split of the scan (8, 4 or 2)
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* g_raw;
+  const void* beta_raw;
+  int g_dtype, beta_dtype;
+  const int32_t* d_cu;     // [N+1] token bounds (device)
+  const int32_t* d_co;     // [N+1] chunk offsets (device)
+  const int32_t* d_table;  // [n_chunks][2] (sequence, chunk within sequence) (device)
+  int state_dtype;
+  const void* state_in;
+  int in_mode;
+  void* state_out;
+  int out_mode;
+  int64_t stride0;  // elements between sequence/slot planes
+  const int32_t* indices;
+  const uint8_t* flags;
+  void* out;
+  void* ws;
+};
+
+// Launchers (defined in the .hip files). Return 0 on success, nonzero HIP error code.
+int launch_prep(const Plan& p, void* stream);
+int launch_scan(const Plan& p, void* stream);
+
+}  // namespace kda

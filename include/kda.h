@@ -1,0 +1,200 @@
+/*
+ * kda.h: C ABI of the MI355X (gfx950) chunkwise Kimi Delta Attention prefill library.
+ *
+ * Operation (aiter PR 4741, "[FlyDSL] Add gfx950 Kimi Delta Attention prefill kernel",
+ * Summary and Optimizations Applied): for every token t of sequence n and head h, with
+ * a V-first state S in R^{V x K} (K = V = 128),
+ *
+ *     q^ = q / sqrt(|q|^2 + 1e-6),  k^ = k / sqrt(|k|^2 + 1e-6)
+ *     g  = lower_bound * sigmoid(g_raw)        (one value per key channel)
+ *     b  = sigmoid(beta_raw)                   (one value per token-head)
+ *     S  = S Diag(exp g) (I - b k^ k^T) + b v k^T
+ *     o  = scale * S q^
+ *
+ * computed chunkwise (32-token chunks) by three stages on the caller's stream: host
+ * metadata, a chunk-parallel prep kernel (L2-norm, gate, beta, in-chunk gate cumsum,
+ * bounded intra-chunk tiles, the unit-lower-triangular solve and the w/u products) and
+ * a serial scan kernel over each sequence's chunks that carries the fp32 state.
+ *
+ * State I/O follows aiter PR 5754 (FlashKDA paged state_cache, Technical Details): a
+ * dense initial/final state, or a paged pool [slots, H, V, K] whose slot planes are
+ * dense and whose stride(0) may be padded, addressed by int32 state_indices with a
+ * per-sequence has_initial_state flag. Stored state may be fp32, fp16 or bf16 and is
+ * accumulated in fp32 (aiter PR 5249, What). Host bounds (cu_seqlens_host) let the
+ * call build and upload its metadata without any synchronising call (aiter PR 6912,
+ * Changes).
+ *
+ * Conventions for every function below:
+ *  - Pointers are device memory owned by the caller unless marked "host".
+ *  - The library never allocates or frees caller memory. It owns only its context:
+ *    pinned staging buffers and a device-side metadata cache.
+ *  - Tensors are contiguous row-major with the shapes stated; "[T, H, D]" means
+ *    element (t, h, d) sits at offset (t * H + h) * D + d.
+ *  - A failed call returns before enqueuing any work: nothing is written.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+typedef enum kda_status {
+  KDA_OK = 0,
+  KDA_ERR_INVALID_ARG = 1,  /* null required pointer, N < 1, T < 0, bad bounds, non-finite scale */
+  KDA_ERR_UNSUPPORTED = 2,  /* K or V != 128, dtype not allowed, lower_bound > 0, not gfx950 */
+  KDA_ERR_STATE_MODE = 3,   /* dense and paged state both given, or final_state with a pool */
+  KDA_ERR_STRIDE = 4,       /* state_cache_stride0 < H*V*K */
+  KDA_ERR_ALIAS = 5,        /* the byte ranges of out and v overlap */
+  KDA_ERR_WORKSPACE = 6,    /* workspace null or smaller than kda_chunk_fwd_workspace_bytes() */
+  KDA_ERR_CAPTURE_MISS = 7, /* metadata-cache miss while the stream is being captured */
+  KDA_ERR_HIP = 8           /* a HIP runtime call or a kernel launch failed */
+} kda_status;
+
+/* Element types accepted by the arguments that allow a choice. */
+typedef enum kda_dtype { KDA_F32 = 0, KDA_F16 = 1, KDA_BF16 = 2 } kda_dtype;
+
+/* Arguments of one forward call. Zero-initialise, then fill. */
+typedef struct kda_fwd_args {
+  int32_t T; /* total tokens over all sequences (batch 1, packed varlen); may be 0 */
+  int32_t N; /* number of sequences, >= 1 */
+  int32_t H; /* heads, >= 1 */
+  int32_t K; /* key head size, must be 128 */
+  int32_t V; /* value head size, must be 128 */
+  float scale;       /* read-out scale, finite; 1/sqrt(K) is the usual value */
+  float lower_bound; /* gate lower bound, finite and <= 0 (the pages use -5) */
+
+  const void* q;        /* bf16 [T, H, K] */
+  const void* k;        /* bf16 [T, H, K] */
+  const void* v;        /* bf16 [T, H, V] */
+  const void* g_raw;    /* [T, H, K], dtype g_dtype (KDA_F32 or KDA_BF16): raw gate */
+  const void* beta_raw; /* [T, H], dtype beta_dtype (KDA_F32 or KDA_BF16): raw beta */
+  kda_dtype g_dtype;
+  kda_dtype beta_dtype;
+
+  const int32_t* cu_seqlens;      /* [N+1] device sequence bounds, cu[0] = 0, cu[N] = T */
+  const int32_t* cu_seqlens_host; /* [N+1] host copy, nullable. Trusted to equal the device
+                                     copy and never compared with it. With it the call makes
+                                     no synchronising call; without it the bounds are read
+                                     back once (one counted stream synchronisation). */
+
+  /* State, exactly one of three modes:
+   *   none : all state pointers null -> zero initial state, no final state;
+   *   dense: initial_state and/or final_state set (state_cache null);
+   *   paged: state_cache set (initial_state and final_state null). */
+  kda_dtype state_dtype;     /* element type of whichever state tensors are given */
+  const void* initial_state; /* dense [N, H, V, K], nullable (null -> zero) */
+  void* final_state;         /* dense [N, H, V, K], nullable (null -> not written) */
+  void* state_cache;         /* paged pool: slot s plane at state_cache + s*stride0 elements,
+                                laid out [H, V, K]; read and written in place */
+  int64_t num_slots;          /* slots in the pool (>= 1 when paged) */
+  int64_t state_cache_stride0; /* elements between consecutive slots, >= H*V*K */
+  const int32_t* state_indices;      /* [N] device: slot of each sequence. Not validated on the
+                                        device (that would need a sync): out-of-range or
+                                        duplicate indices are undefined behaviour. */
+  const uint8_t* has_initial_state;  /* [N] device bools: 0 -> the sequence starts from zero
+                                        and its slot is not read */
+
+  void* out; /* bf16 [T, H, V], required; must not overlap v */
+} kda_fwd_args;
+
+/* Counters kept per context. */
+typedef struct kda_stats {
+  uint64_t calls;          /* successful kda_chunk_fwd calls */
+  uint64_t cache_hits;     /* metadata found in the cache (no upload) */
+  uint64_t cache_misses;   /* metadata built and uploaded */
+  uint64_t blocking_syncs; /* host waits on the device: bounds read-backs and staging reuse */
+  uint64_t d2h_reads;      /* bounds read back because cu_seqlens_host was null */
+  uint64_t h2d_uploads;    /* asynchronous metadata uploads */
+  int32_t last_dv_split;   /* value-channel split used by the last scan launch */
+  int32_t last_ref_block;  /* reference-row block used by the last prep launch */
+  int64_t last_n_chunks;   /* chunks (over all sequences) in the last call */
+} kda_stats;
+
+typedef struct kda_ctx kda_ctx;
+
+/* ---- Host-runtime seam (for tests). ----------------------------------------------
+ * Every HIP runtime call and kernel launch of the host orchestration goes through this
+ * table. kda_ctx_create() installs the real HIP runtime. A test can install a fake with
+ * kda_ctx_create_with_runtime() to run the host logic (validation, metadata, cache,
+ * uploads, synchronisation accounting, launch sequence) on a machine without a GPU.
+ * Each function returns 0 on success and nonzero on failure; event_query returns 0 when
+ * the event has completed, 1 while it is pending and a negative value on failure. */
+typedef struct kda_runtime {
+  void* user;
+  int (*memcpy_h2d_async)(void* user, void* dst, const void* src, size_t bytes, void* stream);
+  int (*memcpy_d2h_async)(void* user, void* dst, const void* src, size_t bytes, void* stream);
+  int (*stream_synchronize)(void* user, void* stream);
+  int (*stream_is_capturing)(void* user, void* stream, int* capturing);
+  int (*event_create)(void* user, void** event);
+  int (*event_destroy)(void* user, void* event);
+  int (*event_record)(void* user, void* event, void* stream);
+  int (*event_query)(void* user, void* event);
+  int (*event_synchronize)(void* user, void* event);
+  int (*stream_wait_event)(void* user, void* stream, void* event);
+  int (*host_alloc_pinned)(void* user, void** ptr, size_t bytes);
+  int (*host_free_pinned)(void* user, void* ptr);
+  int (*device_alloc)(void* user, void** ptr, size_t bytes);
+  int (*device_free)(void* user, void* ptr);
+  /* kernel: 0 = prep, 1 = scan. plan is internal launch data, opaque to the runtime. */
+  int (*launch)(void* user, int kernel, const void* plan, void* stream);
+} kda_runtime;
+
+/* Context: device properties (CU count), pinned staging ring, metadata cache, stats.
+ * device is a HIP device ordinal. Returns KDA_ERR_UNSUPPORTED on a device that is not
+ * gfx950. One context may be used from one host thread at a time. */
+kda_status kda_ctx_create(int device, kda_ctx** out);
+kda_status kda_ctx_create_with_runtime(const kda_runtime* rt, int cu_count, kda_ctx** out);
+/* Waits for the context's outstanding uploads, then frees what it owns. */
+void kda_ctx_destroy(kda_ctx* ctx);
+
+/* Host-only, pure: bytes of caller workspace one call with these shapes needs
+ * (depends on T, N, H only). 0 when the arguments are invalid. */
+size_t kda_chunk_fwd_workspace_bytes(const kda_fwd_args* args);
+
+/* Host-only: every argument check kda_chunk_fwd makes, touching no device memory. */
+kda_status kda_chunk_fwd_validate(const kda_fwd_args* args);
+
+/* Forward call. Validates, resolves metadata (cache hit, or one asynchronous upload from
+ * pinned memory), then enqueues prep and scan on stream (a hipStream_t; null = default
+ * stream) and returns without waiting. The workspace (caller-owned device memory of at
+ * least kda_chunk_fwd_workspace_bytes(args) bytes, 256-byte aligned) must stay
+ * allocated and unused by anything else until the stream work completes. */
+kda_status kda_chunk_fwd(kda_ctx* ctx, const kda_fwd_args* args, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/* Host-only chunk table (aiter PR 6912, Changes and Tests): for host bounds
+ * cu_host[0..n_seqs], writes pairs (sequence, chunk-within-sequence) of every chunk of
+ * `chunk` tokens, sequences in cu order, an empty sequence contributing none.
+ * pairs_out has room for cap pairs (2*cap int32); *n_out receives the pair count even
+ * when it exceeds cap (then KDA_ERR_INVALID_ARG is returned and nothing is written). */
+kda_status kda_prepare_chunk_indices(const int32_t* cu_host, int32_t n_seqs, int32_t chunk,
+                                     int32_t* pairs_out, int64_t cap, int64_t* n_out);
+
+/* Value-channel split the scan uses for n_seqs sequences of H heads on cu_count compute
+ * units (host-only, pure): the finest split in {8, 4, 2} with n_seqs*H*split <= 2*cu_count,
+ * else 2 (aiter PR 4741, Optimizations Applied: occupancy-aware dv_split). */
+int32_t kda_dv_split(int32_t n_seqs, int32_t H, int32_t cu_count);
+
+/* Reference-row block the prep kernel uses for a gate lower bound (host-only, pure): the
+ * largest s in {16, 8, 4, 2, 1} with (s - 1) * |lower_bound| <= 80, so that every factor
+ * of the intra-chunk decay construction stays within e^{+-80} (aiter PR 4741,
+ * Optimizations Applied: bounded construction, NaN-free to 640 nats). */
+int32_t kda_ref_block(float lower_bound);
+
+/* sizeof(kda_fwd_args), so a binding can check its mirror of the struct. */
+size_t kda_fwd_args_size(void);
+
+const char* kda_status_str(kda_status status);
+kda_status kda_get_stats(const kda_ctx* ctx, kda_stats* out);
+kda_status kda_reset_stats(kda_ctx* ctx);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

@@ -1,0 +1,131 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Bars: output rel-L2 <= 5e-3; final state rel-L2 <= 5e-3 with fp32 state storage and
+<= 1e-2 with fp16 / bf16 storage. Sizes: small cases run the whole oracle (several
+chunks and a ragged tail); the full-size workloads compare every output of a sample of
+heads or sequences the oracle can afford, plus properties checked on everything.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gated_delta_rule_pack_amd.workloads import config, make_workload
+from tests.kda_harness import compare, run_gpu, untouched_slots_bitwise
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def test_cfg1_dense_T256_H1():
+    wl = config(1)
+    _say(f"case {wl.name}")
+    run = run_gpu(wl)
+    e_out, e_state = compare(wl, run)
+    _say(f"  out {e_out:.3e} state {e_state:.3e}")
+
+
+@pytest.mark.parametrize("state_dtype", ["f32", "f16", "bf16"])
+def test_small_varlen_paged_mixed_flags(state_dtype):
+    """Ragged lengths (empty, 1, 31, 32, 33, ...), mixed flags, NaN-poisoned unread slots."""
+    wl = make_workload("small_varlen", [1, 31, 0, 32, 33, 95, 0, 64, 7], H=3, seed=11,
+                       state_mode="paged", state_dtype=state_dtype, num_slots=13, stride_pad=64,
+                       has_initial="bernoulli")
+    _say(f"case {wl.name} {state_dtype} flags={wl.has_initial_state.tolist()}")
+    run = run_gpu(wl)
+    e_out, e_state = compare(wl, run)
+    untouched_slots_bitwise(wl, run)
+    _say(f"  out {e_out:.3e} state {e_state:.3e}")
+
+
+@pytest.mark.parametrize("state_dtype", ["f32", "f16", "bf16"])
+def test_small_dense_state_dtypes(state_dtype):
+    wl = make_workload("small_dense", [70, 5, 128], H=2, seed=12, state_mode="dense",
+                       state_dtype=state_dtype)
+    _say(f"case {wl.name} {state_dtype}")
+    run = run_gpu(wl)
+    assert run.final_state is not None
+    e_out, e_state = compare(wl, run)
+    _say(f"  out {e_out:.3e} state {e_state:.3e}")
+
+
+def test_no_state_mode():
+    wl = make_workload("nostate", [40, 0, 90], H=2, seed=13, state_mode="none")
+    run = run_gpu(wl)
+    e_out, _ = compare(wl, run)
+    _say(f"  out {e_out:.3e}")
+
+
+def test_bf16_gate_and_beta_inputs():
+    wl = make_workload("bf16_raw", [77, 33], H=2, seed=14, state_mode="dense", gate_dtype="bf16",
+                       beta_dtype="bf16")
+    run = run_gpu(wl)
+    e_out, e_state = compare(wl, run)
+    _say(f"  out {e_out:.3e} state {e_state:.3e}")
+
+
+@pytest.mark.parametrize("lb,shift", [(-5.0, 6.0), (-20.0, 6.0), (-1.0, -4.0), (0.0, 0.0), (-100.0, 0.0)])
+def test_gate_regimes_ref_blocks(lb, shift):
+    """Saturated gates (160 / 640 nats per chunk), weak decay, no decay, huge decay."""
+    wl = make_workload("gates", [100, 64], H=2, seed=15, state_mode="dense", lower_bound=lb, gate_shift=shift)
+    run = run_gpu(wl)
+    e_out, e_state = compare(wl, run)
+    _say(f"  lb {lb} shift {shift}: out {e_out:.3e} state {e_state:.3e}")
+
+
+def test_cfg2_1x4096_H12_paged_full():
+    wl = config(2)
+    _say(f"case {wl.name}")
+    run = run_gpu(wl)
+    e_out, e_state = compare(wl, run)
+    untouched_slots_bitwise(wl, run)
+    _say(f"  out {e_out:.3e} state {e_state:.3e}")
+
+
+def test_cfg3_1x16384_H12_padded_stride_sampled_heads():
+    wl = config(3)
+    _say(f"case {wl.name}")
+    run = run_gpu(wl)
+    assert np.all(np.isfinite(run.out))
+    e_out, e_state = compare(wl, run, heads=[0, 7])
+    untouched_slots_bitwise(wl, run)
+    _say(f"  heads 0,7: out {e_out:.3e} state {e_state:.3e}")
+
+
+@pytest.mark.parametrize("lb,shift", [(-5.0, 6.0), (-20.0, 6.0)])
+def test_cfg3_saturated_gates_nan_free(lb, shift):
+    """~160 nats (lb -5, raw +6) and ~640 nats (lb -20) of decay per chunk stay NaN-free."""
+    wl = config(3, gate_shift=shift, lower_bound=lb)
+    _say(f"case {wl.name} lb={lb} shift={shift}")
+    run = run_gpu(wl)
+    assert np.all(np.isfinite(run.out))
+    e_out, e_state = compare(wl, run, heads=[3])
+    _say(f"  head 3: out {e_out:.3e} state {e_state:.3e}")
+
+
+def test_cfg4_varlen128_sampled_sequences():
+    wl = config(4)
+    lens = wl.info["lengths"]
+    flags = wl.has_initial_state.tolist()
+    empties = [i for i, x in enumerate(lens) if x == 0][:2]
+    no_init = [i for i, f in enumerate(flags) if not f and lens[i] > 0][:3]
+    longest = [int(np.argmax(lens))]
+    sample = sorted(set(empties + no_init + longest + [0, 1, len(lens) - 1]))
+    _say(f"case {wl.name} T={wl.T} sample={sample}")
+    run = run_gpu(wl)
+    assert np.all(np.isfinite(run.out))
+    e_out, e_state = compare(wl, run, seqs=sample)
+    untouched_slots_bitwise(wl, run)
+    _say(f"  out {e_out:.3e} state {e_state:.3e}")
+
+
+@pytest.mark.parametrize("state_dtype", ["bf16", "f16"])
+def test_cfg5_decode_like_state_bound(state_dtype):
+    wl = config(5, state_dtype=state_dtype)
+    _say(f"case {wl.name} {state_dtype}")
+    run = run_gpu(wl)
+    e_out, e_state = compare(wl, run)
+    untouched_slots_bitwise(wl, run)
+    _say(f"  out {e_out:.3e} state {e_state:.3e}")
