@@ -1,0 +1,265 @@
+#!/usr/bin/env python3
+"""Benchmark chunkwise KDA prefill on one MI355X.
+
+One step = one ``kda_chunk_fwd`` call (metadata lookup, prep kernel, scan kernel) over
+one batch of synthetic input already resident in HBM. The default workload is the
+1 x 4096-token, 12-head call with a paged fp32 state pool (the per-GPU Kimi-K3 serving
+shape); ``--workload`` selects the other shapes.
+
+Prints ONE JSON line with the throughput (tokens/s), the per-call latency, the roofline
+of the dominant kernel (timed live with HIP events on the call's stream) and the fp64
+oracle timed on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "KDA prefill µs/call + tokens/s, H=12 1×4K/1×16K; % of MFMA/HBM peak"
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
+RECORD_BYTES = 35328  # per (head, chunk) workspace record written by prep, read by scan
+
+WORKLOADS = {
+    "cfg2": (2, "1x4096 tokens, H=12, K=V=128, paged fp32 state pool [64,12,128,128]"),
+    "cfg3": (3, "1x16384 tokens, H=12, K=V=128, paged fp32 pool with stride(0) padded by 4096"),
+    "cfg4": (4, "128 varlen sequences (0..2048 tokens, 4 empty), H=12, paged fp32 pool [256,...]"),
+    "cfg5": (5, "256 sequences x 1 token, H=12, paged bf16 pool [512,12,128,128]"),
+}
+
+
+def _oracle_head(args):
+    # Worker: the oracle on one head of the workload (heads are independent).
+    from oracle import kda_forward
+    q, k, v, g, b, cu, scale, lb, S = args
+    return kda_forward(q, k, v, g, b, cu, scale=scale, lower_bound=lb, **S)
+
+
+def cpu_baseline(wl, max_tokens: int, workers: int):
+    """Time the fp64 oracle on a bounded sample of the workload (before any GPU use)."""
+    import multiprocessing as mp
+
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from gated_delta_rule_pack_amd.workloads import to_f64
+
+    cu = wl.cu_seqlens.numpy().astype(np.int64)
+    # Sample: whole sequences in order until max_tokens.
+    take = 1
+    while take < wl.N and cu[take + 1] <= max_tokens:
+        take += 1
+    t_end = int(min(cu[take], max_tokens))
+    cu_s = np.minimum(cu[: take + 1], t_end)
+    q = to_f64(wl.q[0, :t_end]); k = to_f64(wl.k[0, :t_end]); v = to_f64(wl.v[0, :t_end])
+    g = to_f64(wl.g_raw[0, :t_end]); b = to_f64(wl.beta_raw[0, :t_end])
+    tasks = []
+    for h in range(wl.H):
+        S = {}
+        if wl.state_mode == "paged":
+            S = dict(state_cache=to_f64(wl.cache_view()[:, h:h + 1]), state_indices=wl.state_indices.numpy()[:take],
+                     has_initial_state=wl.has_initial_state.numpy()[:take])
+        elif wl.state_mode == "dense":
+            S = dict(initial_state=to_f64(wl.initial_state[:take, h:h + 1]))
+        tasks.append((q[:, h:h + 1], k[:, h:h + 1], v[:, h:h + 1], g[:, h:h + 1], b[:, h:h + 1], cu_s,
+                      wl.scale, wl.lower_bound, S))
+    workers = max(1, min(workers, len(tasks)))
+    with threadpool_limits(1):
+        ctx = mp.get_context("fork")
+        with ctx.Pool(workers) as pool:
+            pool.map(abs, range(workers))  # start the workers before timing
+            t0 = time.perf_counter()
+            pool.map(_oracle_head, tasks, chunksize=1)
+            wall = time.perf_counter() - t0
+    tokens = int(cu_s[-1])
+    return {
+        "value": tokens / wall, "unit": "tokens/s", "cores": workers, "kind": "oracle",
+        "sample": f"first {tokens} tokens ({take} sequence(s)) of the workload, all {wl.H} heads, "
+                  f"one head per worker process, fp64 numpy token loop",
+        "seconds": wall,
+    }
+
+
+def _source_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_from_profiles(kernel: str, workload: str):
+    """HBM bytes per launch from the committed counter summary, if its kernel source matches."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_traffic_{workload}.txt")
+    src = os.path.join(ROOT, "gated_delta_rule_pack_amd", "csrc", f"kda_{kernel}.hip")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_hash = re.search(r"source_sha256_16:\s*([0-9a-f]+)", text)
+    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_bytes or m_hash.group(1) != _source_hash(src):
+        return None
+    return float(m_bytes.group(1))
+
+
+def algorithmic_bytes(wl, kernel: str, n_chunks: int):
+    """Per-launch algorithmic bytes of one kernel (per-unit figures stated in the design notes).
+
+    prep: reads q, k, v (3 x 256 B), raw gate (512 B fp32 / 256 B bf16) and raw beta
+          (4 / 2 B) per valid token-head; writes one 35328-byte record per chunk-head.
+    scan: reads each chunk-head record once; writes 256 B of output per token-head;
+          reads (when the flag is set) and writes one V x K state per sequence-head.
+    call: the method's own bytes: q, k, v, raw gate, raw beta, out per token-head plus the
+          state read/write, no intermediates.
+    """
+    th = wl.T * wl.H
+    g_b = wl.g_raw.element_size() * 128
+    b_b = wl.beta_raw.element_size()
+    s_b = {"f32": 4, "f16": 2, "bf16": 2}[wl.state_dtype] * 128 * 128
+    n_read = wl.N if wl.state_mode != "paged" else int(wl.has_initial_state.sum())
+    if wl.state_mode == "none":
+        n_read = 0
+    n_write = wl.N if wl.state_mode in ("paged", "dense") else 0
+    state = (n_read + n_write) * wl.H * s_b
+    if kernel == "prep":
+        return th * (3 * 256 + g_b + b_b) + n_chunks * wl.H * RECORD_BYTES
+    if kernel == "scan":
+        return n_chunks * wl.H * RECORD_BYTES + th * 256 + state
+    return th * (3 * 256 + g_b + b_b + 256) + state
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="cfg2")
+    ap.add_argument("--rotate", type=int, default=0,
+                    help="input sets cycled through (0: enough to exceed the 256 MB MALL)")
+    ap.add_argument("--cpu-tokens", type=int, default=4096, help="oracle sample size (tokens)")
+    ap.add_argument("--cpu-workers", type=int, default=12)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the KDA path here is single-GPU: heads and sequences shard without communication, "
+              "so per-GPU throughput is the number to read.", file=sys.stderr)
+        sys.exit(2)
+
+    from gated_delta_rule_pack_amd.workloads import config
+    cfg_id, cfg_desc = WORKLOADS[args.workload]
+    wl = config(cfg_id)
+
+    # Oracle baseline on the host first, before anything initialises the GPU.
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, args.cpu_tokens, args.cpu_workers)
+
+    import torch
+
+    import gated_delta_rule_pack_amd as kda
+    from gated_delta_rule_pack_amd import _lib
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    lib = _lib.load()
+    ctx = kda.get_context(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    # Input sets resident in HBM, rotated so the caches cannot hold them between steps.
+    per_set = sum(t.numel() * t.element_size() for t in (wl.q, wl.k, wl.v, wl.g_raw, wl.beta_raw)) + \
+        wl.v.numel() * 2
+    n_rot = args.rotate or max(1, min(8, (512 << 20) // per_set + 1))
+    base = {n: getattr(wl, n).to(dev) for n in ("q", "k", "v", "g_raw", "beta_raw")}
+    cu_d = wl.cu_seqlens.to(dev)
+    cu_h = wl.cu_seqlens.clone()
+    state = {}
+    if wl.state_mode == "paged":
+        storage = wl.state_storage.to(dev)
+        state = dict(state_cache=storage.as_strided((wl.num_slots, wl.H, 128, 128),
+                                                    (wl.state_stride0, 128 * 128, 128, 1)),
+                     state_indices=wl.state_indices.to(dev), has_initial_state=wl.has_initial_state.to(dev))
+    sets = []
+    for i in range(n_rot):
+        s = {n: (t if i == 0 else t.clone()) for n, t in base.items()}
+        s["out"] = torch.empty_like(s["v"])
+        a = kda.make_args(s["q"], s["k"], s["v"], s["g_raw"], s["beta_raw"], cu_d, cu_seqlens_cpu=cu_h,
+                          scale=wl.scale, lower_bound=wl.lower_bound, out=s["out"], **state)
+        rc = lib.kda_chunk_fwd_validate(ctypes.byref(a))
+        if rc != _lib.KDA_OK:
+            raise kda.KDAError(rc, "validate")
+        sets.append((s, a))
+    ws_bytes = kda.workspace_bytes(sets[0][1])
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    ws_p, ws_n, st_p = ctypes.c_void_p(ws.data_ptr()), ctypes.c_size_t(ws_bytes), ctypes.c_void_p(stream.cuda_stream)
+
+    def step(i):
+        rc = lib.kda_chunk_fwd(ctx.ptr, ctypes.byref(sets[i % n_rot][1]), ws_p, ws_n, st_p)
+        if rc != _lib.KDA_OK:
+            raise kda.KDAError(rc, "kda_chunk_fwd")
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ctx.reset_stats()
+    ctx.profile(True)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ctx.profile(False)
+    prep_ms, scan_ms, ncalls = ctx.profile_read()
+    stats = ctx.stats()
+    ms_total = e0.elapsed_time(e1)
+    ms_step = ms_total / args.steps
+    tokens = wl.T
+    value = tokens / (ms_step * 1e-3)
+
+    n_chunks = int(stats["last_n_chunks"])
+    k_us = {"prep": 1e3 * prep_ms / max(ncalls, 1), "scan": 1e3 * scan_ms / max(ncalls, 1)}
+    dom = max(k_us, key=k_us.get)
+    ab = algorithmic_bytes(wl, dom, n_chunks)
+    achieved = ab / (k_us[dom] * 1e-6) / 1e9
+    traffic = traffic_from_profiles(dom, args.workload)
+    call_bytes = algorithmic_bytes(wl, "call", n_chunks)
+    roofline = {
+        "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+        "kernel": f"kda_{dom}", "kernel_us": round(k_us[dom], 2), "algorithmic_bytes": int(ab),
+        "call_algorithmic_bytes": int(call_bytes),
+        "call_frac": round(call_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+    }
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "us_per_call": round(ms_step * 1e3, 2), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": cfg_desc, "T": wl.T, "N": wl.N, "H": wl.H, "K": 128, "V": 128, "chunk": 32,
+                   "lower_bound": wl.lower_bound, "state": f"{wl.state_mode} {wl.state_dtype}",
+                   "dv_split": stats["last_dv_split"], "ref_block": stats["last_ref_block"],
+                   "input_sets_rotated": n_rot, "parallelism": "single GPU"},
+        "kernels_us": {k: round(v, 2) for k, v in k_us.items()},
+        "host_wall_us_per_call": round(wall / args.steps * 1e6, 2),
+        "metadata": {"cache_hits": stats["cache_hits"], "cache_misses": stats["cache_misses"],
+                     "blocking_syncs": stats["blocking_syncs"]},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

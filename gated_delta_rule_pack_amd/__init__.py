@@ -43,6 +43,18 @@ class Context:
     def reset_stats(self) -> None:
         _lib.load().kda_reset_stats(self.ptr)
 
+    def profile(self, enable: bool) -> None:
+        """Record per-kernel timing events in every following call (or stop)."""
+        _lib.load().kda_profile_enable(self.ptr, 1 if enable else 0)
+
+    def profile_read(self):
+        """(prep_ms_total, scan_ms_total, calls) since the last read; waits for the events."""
+        a, b, n = ctypes.c_double(), ctypes.c_double(), ctypes.c_int64()
+        rc = _lib.load().kda_profile_read(self.ptr, ctypes.byref(a), ctypes.byref(b), ctypes.byref(n))
+        if rc != _lib.KDA_OK:
+            raise KDAError(rc, "kda_profile_read")
+        return a.value, b.value, n.value
+
     def close(self) -> None:
         if self.ptr:
             _lib.load().kda_ctx_destroy(self.ptr)

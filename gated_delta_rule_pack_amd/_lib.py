@@ -72,6 +72,7 @@ WAIT = CFUNCTYPE(c_int, c_void_p, c_void_p, c_void_p)
 ALLOC = CFUNCTYPE(c_int, c_void_p, POINTER(c_void_p), c_size_t)
 FREE = CFUNCTYPE(c_int, c_void_p, c_void_p)
 LAUNCH = CFUNCTYPE(c_int, c_void_p, c_int, c_void_p, c_void_p)
+ELAPSED = CFUNCTYPE(c_int, c_void_p, POINTER(c_float), c_void_p, c_void_p)
 
 
 class Runtime(Structure):
@@ -84,6 +85,7 @@ class Runtime(Structure):
         ("host_alloc_pinned", ALLOC), ("host_free_pinned", FREE),
         ("device_alloc", ALLOC), ("device_free", FREE),
         ("launch", LAUNCH),
+        ("event_create_timed", EVCREATE), ("event_elapsed_ms", ELAPSED),
     ]
 
 
@@ -125,6 +127,10 @@ def load() -> ctypes.CDLL:
     lib.kda_get_stats.argtypes = [P, POINTER(Stats)]
     lib.kda_reset_stats.restype = c_int
     lib.kda_reset_stats.argtypes = [P]
+    lib.kda_profile_enable.restype = c_int
+    lib.kda_profile_enable.argtypes = [P, c_int]
+    lib.kda_profile_read.restype = c_int
+    lib.kda_profile_read.argtypes = [P, POINTER(ctypes.c_double), POINTER(ctypes.c_double), POINTER(c_int64)]
     lib.kda_fwd_args_size.restype = c_size_t
     lib.kda_fwd_args_size.argtypes = []
     if lib.kda_fwd_args_size() != ctypes.sizeof(FwdArgs):
@@ -142,5 +148,5 @@ EXPORTS = [
     "kda_ctx_create", "kda_ctx_create_with_runtime", "kda_ctx_destroy",
     "kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd_validate", "kda_chunk_fwd",
     "kda_prepare_chunk_indices", "kda_dv_split", "kda_ref_block", "kda_fwd_args_size",
-    "kda_status_str", "kda_get_stats", "kda_reset_stats",
+    "kda_status_str", "kda_get_stats", "kda_reset_stats", "kda_profile_enable", "kda_profile_read",
 ]

@@ -64,11 +64,15 @@ int rt_launch(void*, int kernel, const void* plan, void* s) {
   const kda::Plan& p = *reinterpret_cast<const kda::Plan*>(plan);
   return kernel == 0 ? kda::launch_prep(p, s) : kda::launch_scan(p, s);
 }
+int rt_ev_create_timed(void*, void** ev) { return (int)hipEventCreate(reinterpret_cast<hipEvent_t*>(ev)); }
+int rt_ev_elapsed(void*, float* ms, void* a, void* b) {
+  return (int)hipEventElapsedTime(ms, (hipEvent_t)a, (hipEvent_t)b);
+}
 
 const kda_runtime kHipRuntime = {nullptr,    rt_h2d,        rt_d2h,         rt_sync,     rt_capturing,
                                  rt_ev_create, rt_ev_destroy, rt_ev_record, rt_ev_query, rt_ev_sync,
                                  rt_wait,    rt_host_alloc, rt_host_free,   rt_dev_alloc, rt_dev_free,
-                                 rt_launch};
+                                 rt_launch,  rt_ev_create_timed, rt_ev_elapsed};
 
 // ------------------------------------------------------------------ metadata
 inline size_t align4(size_t n) { return (n + 3) & ~size_t(3); }  // int32 count -> 16-byte blocks
@@ -179,8 +183,15 @@ struct Graveyard {
   std::vector<std::pair<void*, void*>> uses;
 };
 
+struct ProfileMarks {
+  void* ev[3];  // before prep, between prep and scan, after scan
+};
+
 struct kda_ctx {
   kda_runtime rt{};
+  bool profiling = false;
+  std::vector<ProfileMarks> marks;       // recorded, not yet read
+  std::vector<ProfileMarks> marks_free;  // reusable
   int cu_count = 0;
   std::vector<CacheEntry*> cache;
   std::vector<Graveyard> graveyard;
@@ -454,6 +465,12 @@ void kda_ctx_destroy(kda_ctx* ctx) {
     rt.device_free(rt.user, e->dev);
     delete e;
   }
+  for (auto* v : {&ctx->marks, &ctx->marks_free})
+    for (auto& m : *v)
+      for (void* e : m.ev) {
+        rt.event_synchronize(rt.user, e);
+        rt.event_destroy(rt.user, e);
+      }
   for (auto& g : ctx->graveyard) {
     for (auto& u : g.uses) rt.event_synchronize(rt.user, u.second);
     release_events(ctx, g.uses);
@@ -556,14 +573,54 @@ kda_status kda_chunk_fwd(kda_ctx* ctx, const kda_fwd_args* a, void* ws, size_t w
   p.out = a->out;
   p.ws = ws;
 
+  ProfileMarks pm{};
+  if (ctx->profiling) {
+    if (!ctx->marks_free.empty()) {
+      pm = ctx->marks_free.back();
+      ctx->marks_free.pop_back();
+    } else {
+      for (void*& e : pm.ev)
+        if (rt.event_create_timed(rt.user, &e)) return hip_fail();
+    }
+    ctx->marks.push_back(pm);
+    if (rt.event_record(rt.user, pm.ev[0], stream)) return hip_fail();
+  }
   if (rt.launch(rt.user, 0, &p, stream)) return hip_fail();
+  if (ctx->profiling && rt.event_record(rt.user, pm.ev[1], stream)) return hip_fail();
   if (rt.launch(rt.user, 1, &p, stream)) return hip_fail();
+  if (ctx->profiling && rt.event_record(rt.user, pm.ev[2], stream)) return hip_fail();
   st = record_use(ctx, e, stream);
   if (st != KDA_OK) return st;
   ctx->stats.calls++;
   ctx->stats.last_dv_split = p.dv_split;
   ctx->stats.last_ref_block = p.ref_block;
   ctx->stats.last_n_chunks = e->meta.n_chunks;
+  return KDA_OK;
+}
+
+kda_status kda_profile_enable(kda_ctx* ctx, int enable) {
+  if (!ctx) return KDA_ERR_INVALID_ARG;
+  ctx->profiling = enable != 0;
+  return KDA_OK;
+}
+
+kda_status kda_profile_read(kda_ctx* ctx, double* prep_ms, double* scan_ms, int64_t* calls) {
+  if (!ctx || !prep_ms || !scan_ms || !calls) return KDA_ERR_INVALID_ARG;
+  auto& rt = ctx->rt;
+  double a = 0.0, b = 0.0;
+  for (auto& m : ctx->marks) {
+    if (rt.event_synchronize(rt.user, m.ev[2])) return hip_fail();
+    float x = 0.f, y = 0.f;
+    if (rt.event_elapsed_ms(rt.user, &x, m.ev[0], m.ev[1]) || rt.event_elapsed_ms(rt.user, &y, m.ev[1], m.ev[2]))
+      return hip_fail();
+    a += x;
+    b += y;
+  }
+  *prep_ms = a;
+  *scan_ms = b;
+  *calls = (int64_t)ctx->marks.size();
+  ctx->marks_free.insert(ctx->marks_free.end(), ctx->marks.begin(), ctx->marks.end());
+  ctx->marks.clear();
   return KDA_OK;
 }
 

@@ -142,6 +142,9 @@ typedef struct kda_runtime {
   int (*device_free)(void* user, void* ptr);
   /* kernel: 0 = prep, 1 = scan. plan is internal launch data, opaque to the runtime. */
   int (*launch)(void* user, int kernel, const void* plan, void* stream);
+  /* Timing events (used only while profiling is enabled). */
+  int (*event_create_timed)(void* user, void** event);
+  int (*event_elapsed_ms)(void* user, float* ms, void* start, void* end);
 } kda_runtime;
 
 /* Context: device properties (CU count), pinned staging ring, metadata cache, stats.
@@ -185,6 +188,13 @@ int32_t kda_dv_split(int32_t n_seqs, int32_t H, int32_t cu_count);
  * of the intra-chunk decay construction stays within e^{+-80} (aiter PR 4741,
  * Optimizations Applied: bounded construction, NaN-free to 640 nats). */
 int32_t kda_ref_block(float lower_bound);
+
+/* Per-kernel timing, off by default. While enabled, each kda_chunk_fwd records timing
+ * events on its stream before prep, between prep and scan, and after scan.
+ * kda_profile_read waits for the recorded events, adds up the prep and scan durations
+ * in milliseconds, reports how many calls they cover, and clears them. */
+kda_status kda_profile_enable(kda_ctx* ctx, int enable);
+kda_status kda_profile_read(kda_ctx* ctx, double* prep_ms, double* scan_ms, int64_t* calls);
 
 /* sizeof(kda_fwd_args), so a binding can check its mirror of the struct. */
 size_t kda_fwd_args_size(void);

@@ -1,0 +1,440 @@
+"""CPU tests of the C ABI (no GPU needed): exports, validation, sizing, chunk table,
+and the host orchestration driven through a recording fake runtime.
+
+The fake runtime stands in for HIP: "device" memory is host memory, copies are memmoves,
+events are integers whose completion the test controls, and kernel launches are only
+recorded. This exercises the metadata cache, the pinned staging ring, the no-sync
+contract with host bounds and the capture rules without a GPU.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from gated_delta_rule_pack_amd import _lib
+from oracle import chunk_indices
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+REC = 35328
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_header_exports_match_library(lib):
+    text = open(os.path.join(ROOT, "include", "kda.h")).read()
+    declared = set(re.findall(r"\b(kda_[a-z0-9_]+)\s*\(", text))
+    declared -= {"kda_status", "kda_dtype"}
+    assert declared == set(_lib.EXPORTS), declared ^ set(_lib.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert lib.kda_fwd_args_size() == ctypes.sizeof(_lib.FwdArgs)
+
+
+def test_status_strings(lib):
+    for code in range(9):
+        assert lib.kda_status_str(code)
+
+
+# ---------------------------------------------------------------- validation
+class FakeBufs:
+    """Aligned host buffers whose addresses stand in for device pointers."""
+
+    def __init__(self):
+        self.keep = []
+
+    def buf(self, nbytes, align=256):
+        raw = np.zeros(nbytes + align, np.uint8)
+        self.keep.append(raw)
+        off = (-raw.ctypes.data) % align
+        return raw[off:off + nbytes]
+
+
+def _valid_args(bufs, T=100, N=3, H=2, paged=False, cu=None):
+    a = _lib.FwdArgs()
+    a.T, a.N, a.H, a.K, a.V = T, N, H, 128, 128
+    a.scale, a.lower_bound = 0.088, -5.0
+    tok = T * H * 128
+    for name, nb in (("q", 2), ("k", 2), ("v", 2), ("g_raw", 4), ("out", 2)):
+        setattr(a, name, bufs.buf(max(tok * nb, 16)).ctypes.data)
+    a.beta_raw = bufs.buf(max(T * H * 4, 16)).ctypes.data
+    a.g_dtype = a.beta_dtype = _lib.KDA_F32
+    if cu is None:
+        cu = np.array([0, 40, 40, T][: N] + [T], np.int32) if N == 3 else np.linspace(0, T, N + 1).astype(np.int32)
+    cu_dev = bufs.buf(4 * (N + 1), 16).view(np.int32)
+    cu_dev[:] = cu
+    cu_host = bufs.buf(4 * (N + 1), 16).view(np.int32)
+    cu_host[:] = cu
+    a.cu_seqlens = cu_dev.ctypes.data
+    a.cu_seqlens_host = cu_host.ctypes.data
+    a.state_dtype = _lib.KDA_F32
+    if paged:
+        a.state_cache = bufs.buf(4 * 4 * H * 128 * 128).ctypes.data
+        a.num_slots = 4
+        a.state_cache_stride0 = H * 128 * 128
+        a.state_indices = bufs.buf(4 * N, 16).ctypes.data
+        a.has_initial_state = bufs.buf(N, 16).ctypes.data
+    return a, cu_dev, cu_host
+
+
+def _check(lib, a):
+    return lib.kda_chunk_fwd_validate(ctypes.byref(a))
+
+
+def test_validation_accepts_valid_args(lib):
+    bufs = FakeBufs()
+    for paged in (False, True):
+        a, _, _ = _valid_args(bufs, paged=paged)
+        assert _check(lib, a) == _lib.KDA_OK
+
+
+@pytest.mark.parametrize("mutate,code", [
+    (lambda a, b: setattr(a, "N", 0), _lib.KDA_ERR_INVALID_ARG),
+    (lambda a, b: setattr(a, "T", -1), _lib.KDA_ERR_INVALID_ARG),
+    (lambda a, b: setattr(a, "K", 64), _lib.KDA_ERR_UNSUPPORTED),
+    (lambda a, b: setattr(a, "V", 256), _lib.KDA_ERR_UNSUPPORTED),
+    (lambda a, b: setattr(a, "scale", float("nan")), _lib.KDA_ERR_INVALID_ARG),
+    (lambda a, b: setattr(a, "lower_bound", 0.5), _lib.KDA_ERR_UNSUPPORTED),
+    (lambda a, b: setattr(a, "g_dtype", _lib.KDA_F16), _lib.KDA_ERR_UNSUPPORTED),
+    (lambda a, b: setattr(a, "state_dtype", 7), _lib.KDA_ERR_UNSUPPORTED),
+    (lambda a, b: setattr(a, "q", None), _lib.KDA_ERR_INVALID_ARG),
+    (lambda a, b: setattr(a, "out", None), _lib.KDA_ERR_INVALID_ARG),
+    (lambda a, b: setattr(a, "cu_seqlens", None), _lib.KDA_ERR_INVALID_ARG),
+    (lambda a, b: setattr(a, "q", a.q + 2), _lib.KDA_ERR_INVALID_ARG),  # misaligned
+    (lambda a, b: setattr(a, "out", a.v), _lib.KDA_ERR_ALIAS),
+    (lambda a, b: setattr(a, "out", a.v + 16 * 1024), _lib.KDA_ERR_ALIAS),  # partial overlap
+    (lambda a, b: setattr(a, "state_cache_stride0", 2 * 128 * 128 - 1), _lib.KDA_ERR_STRIDE),
+    (lambda a, b: setattr(a, "initial_state", b.buf(64).ctypes.data), _lib.KDA_ERR_STATE_MODE),
+    (lambda a, b: setattr(a, "final_state", b.buf(64).ctypes.data), _lib.KDA_ERR_STATE_MODE),
+    (lambda a, b: setattr(a, "state_indices", None), _lib.KDA_ERR_INVALID_ARG),
+    (lambda a, b: setattr(a, "has_initial_state", None), _lib.KDA_ERR_INVALID_ARG),
+    (lambda a, b: setattr(a, "num_slots", 0), _lib.KDA_ERR_INVALID_ARG),
+])
+def test_validation_errors(lib, mutate, code):
+    bufs = FakeBufs()
+    a, _, _ = _valid_args(bufs, paged=True)
+    mutate(a, bufs)
+    assert _check(lib, a) == code
+    assert lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(a)) == 0
+
+
+def test_validation_rejects_inconsistent_host_bounds(lib):
+    bufs = FakeBufs()
+    for bad in ([0, 50, 40, 100], [1, 40, 60, 100], [0, 40, 60, 99]):
+        a, _, host = _valid_args(bufs)
+        host[:] = bad
+        assert _check(lib, a) == _lib.KDA_ERR_INVALID_ARG
+
+
+def test_padded_stride_and_zero_tokens_accepted(lib):
+    bufs = FakeBufs()
+    a, _, _ = _valid_args(bufs, paged=True)
+    a.state_cache_stride0 = 2 * 128 * 128 + 4096
+    assert _check(lib, a) == _lib.KDA_OK
+    a.state_cache_stride0 = 2 * 128 * 128 + 3  # breaks the 16-byte alignment of every slot plane
+    assert _check(lib, a) == _lib.KDA_ERR_INVALID_ARG
+    z, _, _ = _valid_args(bufs, T=0, N=2, cu=np.array([0, 0, 0], np.int32))
+    z.q = z.k = z.v = z.g_raw = z.beta_raw = z.out = None
+    assert _check(lib, z) == _lib.KDA_OK
+
+
+def test_workspace_bytes(lib):
+    bufs = FakeBufs()
+    for T, N, H in [(100, 3, 2), (4096, 1, 12), (0, 2, 1), (1, 1, 1)]:
+        cu = np.linspace(0, T, N + 1).astype(np.int32)
+        a, _, _ = _valid_args(bufs, T=T, N=N, H=H, cu=cu)
+        if T == 0:
+            a.q = a.k = a.v = a.g_raw = a.beta_raw = a.out = None
+        assert lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(a)) == H * ((T + 31) // 32 + N) * REC
+
+
+# ---------------------------------------------------------------- chunk table, policies
+def _chunk_table(lib, cu, chunk=32):
+    cu = np.ascontiguousarray(cu, np.int32)
+    n = ctypes.c_int64()
+    rc = lib.kda_prepare_chunk_indices(cu.ctypes.data, len(cu) - 1, chunk, None, 0, ctypes.byref(n))
+    out = np.zeros((max(n.value, 1), 2), np.int32)
+    rc2 = lib.kda_prepare_chunk_indices(cu.ctypes.data, len(cu) - 1, chunk, out.ctypes.data, n.value,
+                                        ctypes.byref(n))
+    assert rc2 == _lib.KDA_OK
+    return rc, out[: n.value]
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_chunk_table_matches_repeat_interleave_reference(lib, seed):
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(0, 200, size=rng.integers(1, 40))
+    lens[rng.random(lens.size) < 0.3] = 0  # plenty of empty sequences, also before non-empty ones
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    rc, got = _chunk_table(lib, cu)
+    assert np.array_equal(got, chunk_indices(cu, 32))
+    if got.shape[0] > 0:
+        assert rc == _lib.KDA_ERR_INVALID_ARG  # first call had cap 0: reports the count only
+
+
+def test_dv_split_and_ref_block_policies(lib):
+    assert lib.kda_dv_split(1, 12, 256) == 8
+    assert lib.kda_dv_split(4, 12, 256) == 8
+    assert lib.kda_dv_split(8, 12, 256) == 4
+    assert lib.kda_dv_split(16, 12, 256) == 2
+    assert lib.kda_dv_split(128, 12, 256) == 2
+    assert lib.kda_ref_block(-5.0) == 16
+    assert lib.kda_ref_block(-5.4) == 8
+    assert lib.kda_ref_block(-20.0) == 4
+    assert lib.kda_ref_block(0.0) == 16
+    assert lib.kda_ref_block(-200.0) == 1
+
+
+# ---------------------------------------------------------------- fake runtime
+class FakeRuntime:
+    def __init__(self):
+        self.log = []
+        self.next_ev = 1
+        self.pending = set()  # events not yet complete
+        self.capturing = set()
+        self.alloc = {}
+        self.uploads = []
+        self.launches = []
+        rt = _lib.Runtime()
+        rt.user = None
+        self._cbs = dict(
+            memcpy_h2d_async=_lib.H2D(self._h2d), memcpy_d2h_async=_lib.D2H(self._d2h),
+            stream_synchronize=_lib.SYNC(self._sync), stream_is_capturing=_lib.CAPT(self._capt),
+            event_create=_lib.EVCREATE(self._ev_create), event_destroy=_lib.EVONE(self._ev_destroy),
+            event_record=_lib.EVREC(self._ev_record), event_query=_lib.EVONE(self._ev_query),
+            event_synchronize=_lib.EVONE(self._ev_sync), stream_wait_event=_lib.WAIT(self._wait),
+            host_alloc_pinned=_lib.ALLOC(self._halloc), host_free_pinned=_lib.FREE(self._hfree),
+            device_alloc=_lib.ALLOC(self._dalloc), device_free=_lib.FREE(self._dfree),
+            launch=_lib.LAUNCH(self._launch), event_create_timed=_lib.EVCREATE(self._ev_create),
+            event_elapsed_ms=_lib.ELAPSED(self._elapsed))
+        for k, v in self._cbs.items():
+            setattr(rt, k, v)
+        self.rt = rt
+
+    def _h2d(self, user, dst, src, n, s):
+        ctypes.memmove(dst, src, n)
+        self.uploads.append((dst, n, s, np.frombuffer(ctypes.string_at(src, n), np.int32).copy()))
+        self.log.append(("h2d", s))
+        return 0
+
+    def _d2h(self, user, dst, src, n, s):
+        ctypes.memmove(dst, src, n)
+        self.log.append(("d2h", s))
+        return 0
+
+    def _sync(self, user, s):
+        self.log.append(("stream_sync", s))
+        self.pending.clear()
+        return 0
+
+    def _capt(self, user, s, out):
+        out[0] = 1 if s in self.capturing else 0
+        return 0
+
+    def _ev_create(self, user, out):
+        out[0] = self.next_ev
+        self.next_ev += 1
+        return 0
+
+    def _ev_destroy(self, user, e):
+        return 0
+
+    def _ev_record(self, user, e, s):
+        self.pending.add(e)
+        self.log.append(("record", e, s))
+        return 0
+
+    def _ev_query(self, user, e):
+        return 1 if e in self.pending else 0
+
+    def _ev_sync(self, user, e):
+        self.log.append(("event_sync", e))
+        self.pending.discard(e)
+        return 0
+
+    def _wait(self, user, s, e):
+        self.log.append(("wait", s, e))
+        return 0
+
+    def _halloc(self, user, out, n):
+        buf = ctypes.create_string_buffer(n)
+        out[0] = ctypes.addressof(buf)
+        self.alloc[out[0]] = buf
+        self.log.append(("host_alloc", n))
+        return 0
+
+    def _hfree(self, user, p):
+        self.alloc.pop(p, None)
+        return 0
+
+    def _dalloc(self, user, out, n):
+        buf = ctypes.create_string_buffer(n)
+        out[0] = ctypes.addressof(buf)
+        self.alloc[out[0]] = buf
+        self.log.append(("dev_alloc", n))
+        return 0
+
+    def _dfree(self, user, p):
+        self.alloc.pop(p, None)
+        self.log.append(("dev_free", p))
+        return 0
+
+    def _launch(self, user, k, plan, s):
+        self.launches.append((k, s))
+        return 0
+
+    def _elapsed(self, user, out, a, b):
+        out[0] = 1.0
+        return 0
+
+    def syncs(self):
+        return [e for e in self.log if e[0] in ("stream_sync", "event_sync")]
+
+    def complete_all(self):
+        self.pending.clear()
+
+
+@pytest.fixture
+def fake(lib):
+    f = FakeRuntime()
+    ctx = ctypes.c_void_p()
+    assert lib.kda_ctx_create_with_runtime(ctypes.byref(f.rt), 256, ctypes.byref(ctx)) == _lib.KDA_OK
+    f.ctx = ctx
+    yield f
+    lib.kda_ctx_destroy(ctx)
+
+
+def _call(lib, fake, a, stream=0x10, ws=None):
+    bufs = FakeBufs()
+    need = lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(a))
+    ws = ws if ws is not None else bufs.buf(max(need, 256))
+    return lib.kda_chunk_fwd(fake.ctx, ctypes.byref(a), ws.ctypes.data, ws.nbytes, stream)
+
+
+def _stats(lib, fake):
+    s = _lib.Stats()
+    lib.kda_get_stats(fake.ctx, ctypes.byref(s))
+    return s.as_dict()
+
+
+def test_host_bounds_issue_no_sync_and_one_upload(lib, fake):
+    bufs = FakeBufs()
+    a, _, host = _valid_args(bufs, T=300, N=4, cu=np.array([0, 0, 100, 100, 300], np.int32), paged=True)
+    assert _call(lib, fake, a) == _lib.KDA_OK
+    assert fake.syncs() == []
+    assert [e[0] for e in fake.log].count("h2d") == 1
+    assert [e[0] for e in fake.log].count("d2h") == 0
+    assert fake.launches == [(0, 0x10), (1, 0x10)]
+    # The uploaded buffer: cu, per-sequence chunk offsets, chunk table (16-byte aligned blocks).
+    words = fake.uploads[0][3]
+    N = 4
+    cu = words[:N + 1]
+    co = words[8:8 + N + 1]
+    table = words[16:16 + 2 * 11].reshape(-1, 2)
+    assert list(cu) == [0, 0, 100, 100, 300]
+    assert list(co) == [0, 0, 4, 4, 11]
+    ref = chunk_indices(cu, 32)
+    assert np.array_equal(table[: ref.shape[0]], ref)
+    st = _stats(lib, fake)
+    assert st["cache_misses"] == 1 and st["cache_hits"] == 0 and st["blocking_syncs"] == 0
+    # Same bounds again: cache hit, no upload, still no sync.
+    assert _call(lib, fake, a) == _lib.KDA_OK
+    assert [e[0] for e in fake.log].count("h2d") == 1
+    assert fake.syncs() == []
+    st = _stats(lib, fake)
+    assert st["cache_hits"] == 1 and st["calls"] == 2 and st["last_n_chunks"] == 11
+
+
+def test_device_bounds_read_back_once(lib, fake):
+    bufs = FakeBufs()
+    a, _, _ = _valid_args(bufs, T=100, N=3)
+    a.cu_seqlens_host = None
+    assert _call(lib, fake, a) == _lib.KDA_OK
+    kinds = [e[0] for e in fake.log]
+    assert kinds.count("d2h") == 1 and kinds.count("stream_sync") == 1
+    st = _stats(lib, fake)
+    assert st["d2h_reads"] == 1 and st["blocking_syncs"] == 1
+
+
+def test_capture_miss_is_an_error_and_hit_is_retained(lib, fake):
+    bufs = FakeBufs()
+    a, _, _ = _valid_args(bufs, T=100, N=3)
+    fake.capturing.add(0x20)
+    assert _call(lib, fake, a, stream=0x20) == _lib.KDA_ERR_CAPTURE_MISS
+    assert fake.launches == []
+    # Populate the cache outside capture, then hit it under capture.
+    assert _call(lib, fake, a, stream=0x10) == _lib.KDA_OK
+    fake.complete_all()
+    assert _call(lib, fake, a, stream=0x20) == _lib.KDA_OK
+    # Retained: flood the cache with other bounds; the captured entry must survive.
+    for i in range(80):
+        b, _, _ = _valid_args(bufs, T=100 + i, N=1, cu=np.array([0, 100 + i], np.int32))
+        assert _call(lib, fake, b) == _lib.KDA_OK
+        fake.complete_all()
+    n_up = [e[0] for e in fake.log].count("h2d")
+    assert _call(lib, fake, a, stream=0x20) == _lib.KDA_OK  # still a hit under capture
+    assert [e[0] for e in fake.log].count("h2d") == n_up
+    # Without host bounds a read-back would have to run under capture: refused.
+    a.cu_seqlens_host = None
+    assert _call(lib, fake, a, stream=0x20) == _lib.KDA_ERR_CAPTURE_MISS
+
+
+def test_cross_stream_hit_waits_on_upload(lib, fake):
+    bufs = FakeBufs()
+    a, _, _ = _valid_args(bufs, T=100, N=3)
+    assert _call(lib, fake, a, stream=0x10) == _lib.KDA_OK
+    up_ev = [e for e in fake.log if e[0] == "record"][0][1]
+    assert _call(lib, fake, a, stream=0x30) == _lib.KDA_OK
+    waits = [e for e in fake.log if e[0] == "wait"]
+    assert waits == [("wait", 0x30, up_ev)]
+    assert fake.syncs() == []
+
+
+def test_cache_eviction_frees_only_completed_buffers(lib, fake):
+    bufs = FakeBufs()
+    for i in range(70):  # more than the cache holds
+        b, _, _ = _valid_args(bufs, T=50 + i, N=1, cu=np.array([0, 50 + i], np.int32))
+        assert _call(lib, fake, b) == _lib.KDA_OK
+    # Nothing completed yet: evicted buffers wait in the graveyard, none freed, no syncs.
+    assert [e for e in fake.log if e[0] == "dev_free"] == []
+    assert fake.syncs() == [] or all(e[0] == "event_sync" for e in fake.syncs())
+    fake.complete_all()
+    b, _, _ = _valid_args(bufs, T=999, N=1, cu=np.array([0, 999], np.int32))
+    assert _call(lib, fake, b) == _lib.KDA_OK
+    assert len([e for e in fake.log if e[0] == "dev_free"]) >= 6
+
+
+def test_staging_reuse_waits_only_when_copy_pending(lib, fake):
+    bufs = FakeBufs()
+    for i in range(40):  # more misses than staging slots, none completed
+        b, _, _ = _valid_args(bufs, T=10 + i, N=1, cu=np.array([0, 10 + i], np.int32))
+        assert _call(lib, fake, b) == _lib.KDA_OK
+    st = _stats(lib, fake)
+    assert st["blocking_syncs"] == 40 - 32  # one wait per reuse of a busy slot
+    assert st["cache_misses"] == 40
+
+
+def test_workspace_too_small_is_rejected_before_any_work(lib, fake):
+    bufs = FakeBufs()
+    a, _, _ = _valid_args(bufs, T=100, N=3)
+    need = lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(a))
+    ws = bufs.buf(need - 256)
+    assert _call(lib, fake, a, ws=ws) == _lib.KDA_ERR_WORKSPACE
+    assert fake.log == [] and fake.launches == []
+
+
+def test_profiling_hook_reads_and_clears(lib, fake):
+    bufs = FakeBufs()
+    a, _, _ = _valid_args(bufs, T=100, N=3)
+    lib.kda_profile_enable(fake.ctx, 1)
+    for _ in range(3):
+        assert _call(lib, fake, a) == _lib.KDA_OK
+    p, s, n = ctypes.c_double(), ctypes.c_double(), ctypes.c_int64()
+    assert lib.kda_profile_read(fake.ctx, ctypes.byref(p), ctypes.byref(s), ctypes.byref(n)) == _lib.KDA_OK
+    assert n.value == 3 and p.value == 3.0 and s.value == 3.0
+    assert lib.kda_profile_read(fake.ctx, ctypes.byref(p), ctypes.byref(s), ctypes.byref(n)) == _lib.KDA_OK
+    assert n.value == 0
