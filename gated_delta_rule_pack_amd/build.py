@@ -25,6 +25,9 @@ ARCH = "gfx950"
 COMMON_FLAGS = [
     "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # Keep MFMA accumulators in VGPRs: the kernels apply VALU work (decay, conversions)
+    # to them every step, which AGPR accumulators would pay for in copies.
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]

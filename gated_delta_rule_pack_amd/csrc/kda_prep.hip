@@ -1,15 +1,15 @@
 // Chunk-parallel prep kernel for chunkwise KDA prefill on gfx950.
 //
-// One workgroup (4 waves) per (chunk, head). It fuses the pre-processing the pages
-// describe as a separate pack pass (aiter PR 4741, Optimizations Applied: q/k L2 norm,
-// lower-bounded sigmoid gate, beta sigmoid, zero padding as an exact no-op) with the
-// chunk-parallel prep (same page, Summary: "prep, parallel over chunks"):
+// Each (chunk, head) item fuses the pre-processing the pages describe as a separate pack
+// pass (aiter PR 4741, Optimizations Applied: q/k L2 norm, lower-bounded sigmoid gate,
+// beta sigmoid, zero padding as an exact no-op) with the chunk-parallel prep (same page,
+// Summary: "prep, parallel over chunks"):
 //
 //   G      inclusive in-chunk cumsum of g = lb * sigmoid(g_raw), per key channel;
 //          padding rows have g = 0 so they carry the last valid row's G
 //   A      A[r,i] = beta_r sum_c k_r k_i e^{G_r - G_i}          (i < r)
 //   P      P[r,i] = scale sum_c q_r k_i e^{G_r - G_i}           (i <= r)
-//   T      (I + A)^{-1}, unit lower triangular, forward substitution in fp32
+//   T      (I + A)^{-1}, unit lower triangular, fp32
 //   W, U   T diag(beta) (k * e^G),  T diag(beta) v
 //   Q, K   scale * q * e^G,  k * e^{G_C - G};  E = e^{G_C}
 //
@@ -21,6 +21,10 @@
 // inside fp32/bf16 range; factors of earlier rows are <= 1 and may only underflow.
 // The products run on bf16 MFMA with hi/lo operand splits and fp32 accumulation.
 //
+// Organisation: a persistent grid (two workgroups per CU) walks the items; each
+// workgroup loads the next item's inputs while it computes the current one. Thread
+// (wave w, lane l) owns rows 8w .. 8w+7 and key/value channels 2l, 2l+1, so the in-chunk
+// cumsum is mostly in registers and transposed tiles are written 16 bytes at a time.
 // Output: one record per (head, chunk) in the scan's MFMA fragment order.
 
 #include <hip/hip_runtime.h>
@@ -31,52 +35,92 @@
 namespace kda {
 namespace {
 
-constexpr int LDA = 136;  // bf16 per row of a [32][128] operand tile (16-byte pad)
-constexpr int LDT = 40;   // bf16 per row of a transposed [128][32] tile
-constexpr int LDS_F = 36; // fp32 per row of the [32][32] A / P tiles
+constexpr int LDA = 136;   // bf16 per row of a [32][128] operand tile (16-byte pad)
+constexpr int LDT = 40;    // bf16 per row of a transposed [128][32] tile
+constexpr int LDF = 36;    // fp32 per row of the [32][32] A / P / T tiles
 
-constexpr int kOffG = 0;                           // fp32 [32][128]
-constexpr int kOffBeta = kOffG + 32 * 128 * 4;     // fp32 [32]
-constexpr int kOffA = kOffBeta + 32 * 4;           // fp32 [32][LDS_F]
-constexpr int kOffP = kOffA + 32 * LDS_F * 4;      // fp32 [32][LDS_F]
-constexpr int kOffX = kOffP + 32 * LDS_F * 4;      // union region
-constexpr int kTileA = 32 * LDA * 2;               // 8704 B
-constexpr int kTileT = 128 * LDT * 2;              // 10240 B
-constexpr int kTileTT = 32 * LDT * 2;              // 2560 B
-// Phase "factors": left factors (k and q, hi/lo) and right factors (hi/lo).
-constexpr int kOffLKh = kOffX, kOffLKl = kOffLKh + kTileA, kOffLQh = kOffLKl + kTileA,
-              kOffLQl = kOffLQh + kTileA, kOffRh = kOffLQl + kTileA, kOffRl = kOffRh + kTileA;
-// Phase "products": transposed k*e^G (hi/lo), Q staging, transposed K staging,
-// transposed v, T diag(beta) (hi/lo).
-constexpr int kOffKGh = kOffX, kOffKGl = kOffKGh + kTileT, kOffQs = kOffKGl + kTileT,
-              kOffKt = kOffQs + kTileA, kOffVt = kOffKt + kTileT, kOffTh = kOffVt + kTileT,
-              kOffTl = kOffTh + kTileTT;
-constexpr int kEndFactors = kOffRl + kTileA;
-constexpr int kEndProducts = kOffTl + kTileTT;
-constexpr int kLdsBytes = (kEndFactors > kEndProducts ? kEndFactors : kEndProducts);
-static_assert(kLdsBytes <= 80 * 1024, "two workgroups per CU");
+// Region A: small per-item tiles.
+constexpr int kOffTot = 0;                      // fp32 [4][128] per-wave cumsum totals
+constexpr int kOffBeta = kOffTot + 4 * 128 * 4; // fp32 [32]
+constexpr int kOffA = kOffBeta + 32 * 4;        // fp32 [32][LDF]
+constexpr int kOffP = kOffA + 32 * LDF * 4;     // fp32 [32][LDF]
+constexpr int kOffT = kOffP + 32 * LDF * 4;     // fp32 [32][LDF] T = (I + A)^{-1}
+constexpr int kOffM = kOffT + 32 * LDF * 4;     // fp32 [16][LDF] scratch of the block solve
+constexpr int kOffGref = kOffM + 16 * LDF * 4;  // fp32 [32/REF + 1][128] reference rows, then G_C
+// Region X (after Gref): two views.
+constexpr int kTileA = 32 * LDA * 2;            // 8704 B
+constexpr int kTileT = 128 * LDT * 2;           // 10240 B
+constexpr int kTileTT = 32 * LDT * 2;           // 2560 B
+constexpr int kFactorBytes = 6 * kTileA;        // L_k hi/lo, L_q hi/lo, R hi/lo
+constexpr int kProductBytes = 4 * kTileT + kTileA + 2 * kTileTT;  // KG hi/lo, K^T, v^T, Q, T' hi/lo
 
-__device__ __forceinline__ void load_bf16x16(const void* base, size_t elem, float* out) {
-  const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(base) + elem);
-  uint4 a = p[0], b = p[1];
-  uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    out[2 * i] = __uint_as_float(w[i] << 16);
-    out[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-  }
+constexpr int gref_bytes(int ref) { return (32 / ref + 1) * 128 * 4; }
+constexpr int off_x(int ref) { return (kOffGref + gref_bytes(ref) + 255) / 256 * 256; }
+constexpr int lds_bytes(int ref) {
+  return off_x(ref) + (kFactorBytes > kProductBytes ? kFactorBytes : kProductBytes);
+}
+static_assert(lds_bytes(16) <= 80 * 1024, "two workgroups per CU at the default block");
+
+// Offsets inside region X.
+constexpr int xLKh = 0, xLKl = xLKh + kTileA, xLQh = xLKl + kTileA, xLQl = xLQh + kTileA, xRh = xLQl + kTileA,
+              xRl = xRh + kTileA;
+constexpr int xKGh = 0, xKGl = xKGh + kTileT, xKt = xKGl + kTileT, xVt = xKt + kTileT, xQs = xVt + kTileT,
+              xTh = xQs + kTileA, xTl = xTh + kTileTT;
+
+// Inputs of one item held by one thread: rows 8w .. 8w+7, channels 2l, 2l+1.
+struct Inputs {
+  uint32_t q[8], k[8], v[8];  // two bf16 each
+  float2 g[8];                // raw gate (fp32, or bf16 widened on load)
+  float braw;                 // raw beta of row 8w + (lane & 7) (lanes 0..7 meaningful)
+};
+
+struct Item {
+  int cid, h, seq, t0, len;
+};
+
+__device__ __forceinline__ Item item_of(const Plan& p, int item) {
+  Item it;
+  it.cid = item / p.H;
+  it.h = item - it.cid * p.H;
+  it.seq = p.d_table[2 * it.cid];
+  const int jc = p.d_table[2 * it.cid + 1];
+  it.t0 = p.d_cu[it.seq] + kChunk * jc;
+  it.len = min(kChunk, p.d_cu[it.seq + 1] - it.t0);
+  return it;
 }
 
-// Store 16 consecutive bf16 values to LDS (32 bytes, 16-byte aligned).
-__device__ __forceinline__ void st_row16(char* lds, int off, const __bf16* v) {
-  uint4 a, b;
-  const uint16_t* u = reinterpret_cast<const uint16_t*>(v);
-  a.x = u[0] | (uint32_t(u[1]) << 16); a.y = u[2] | (uint32_t(u[3]) << 16);
-  a.z = u[4] | (uint32_t(u[5]) << 16); a.w = u[6] | (uint32_t(u[7]) << 16);
-  b.x = u[8] | (uint32_t(u[9]) << 16); b.y = u[10] | (uint32_t(u[11]) << 16);
-  b.z = u[12] | (uint32_t(u[13]) << 16); b.w = u[14] | (uint32_t(u[15]) << 16);
-  reinterpret_cast<uint4*>(lds + off)[0] = a;
-  reinterpret_cast<uint4*>(lds + off)[1] = b;
+// Loads never depend on a branch (rows past the sequence are clamped into the tensor and
+// masked later) so that the next item's loads can stay in flight during compute.
+__device__ __forceinline__ void load_inputs(const Plan& p, const Item& it, int w, int lane, Inputs& in) {
+  const int H = p.H;
+  const int last = p.T - 1;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int row = min(it.t0 + 8 * w + i, last);
+    const size_t e = ((size_t)row * H + it.h) * kHead + 2 * lane;
+    in.q[i] = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint16_t*>(p.q) + e);
+    in.k[i] = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint16_t*>(p.k) + e);
+    in.v[i] = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint16_t*>(p.v) + e);
+    if (p.g_dtype == kF32) {
+      in.g[i] = *reinterpret_cast<const float2*>(reinterpret_cast<const float*>(p.g_raw) + e);
+    } else {
+      const uint32_t b = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint16_t*>(p.g_raw) + e);
+      in.g[i] = make_float2(__uint_as_float(b << 16), __uint_as_float(b & 0xffff0000u));
+    }
+  }
+  const int brow = min(it.t0 + 8 * w + (lane & 7), last);
+  const size_t bidx = (size_t)brow * H + it.h;
+  in.braw = (p.beta_dtype == kF32) ? reinterpret_cast<const float*>(p.beta_raw)[bidx]
+                                   : bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(p.beta_raw)[bidx]);
+}
+
+__device__ __forceinline__ float lo16(uint32_t x) { return __uint_as_float(x << 16); }
+__device__ __forceinline__ float hi16(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
+__device__ __forceinline__ float rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+__device__ __forceinline__ float sigm(float x) { return rcp(1.0f + __expf(-x)); }
+
+__device__ __forceinline__ uint32_t pack2(__bf16 a, __bf16 b) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
 }
 
 __device__ __forceinline__ bf16x8 ld_frag(const char* lds, int off) {
@@ -84,246 +128,276 @@ __device__ __forceinline__ bf16x8 ld_frag(const char* lds, int off) {
 }
 
 __device__ __forceinline__ bf16x8 ld_frag_2x4(const char* lds, int off0, int off1) {
-  // two 8-byte halves (4 bf16 each)
-  uint2 a = *reinterpret_cast<const uint2*>(lds + off0);
-  uint2 b = *reinterpret_cast<const uint2*>(lds + off1);
-  uint4 r = {a.x, a.y, b.x, b.y};
-  return *reinterpret_cast<bf16x8*>(&r);
+  const uint2 a = *reinterpret_cast<const uint2*>(lds + off0);
+  const uint2 b = *reinterpret_cast<const uint2*>(lds + off1);
+  const uint4 r = {a.x, a.y, b.x, b.y};
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// Write 8 bf16 (one channel, rows 8w .. 8w+7) to a transposed [128][LDT] tile.
+__device__ __forceinline__ void st_col8(char* lds, int off, int c, int w, const __bf16* v) {
+  uint4 x;
+  x.x = pack2(v[0], v[1]);
+  x.y = pack2(v[2], v[3]);
+  x.z = pack2(v[4], v[5]);
+  x.w = pack2(v[6], v[7]);
+  *reinterpret_cast<uint4*>(lds + off + (c * LDT + 8 * w) * 2) = x;
+}
+
+// Sum 16 per-lane values over the 64 lanes of a wave with 17 exchanges: each step keeps
+// half of the values and adds the partner's copy of that half. Lane L ends up holding
+// the total of value index 8*b5 + 4*b4 + 2*b3 + b2 (b = bits of L).
+__device__ __forceinline__ float wave_sum16(const float* x, int lane) {
+  const bool b5 = lane & 32, b4 = lane & 16, b3 = lane & 8, b2 = lane & 4;
+  float y[8], z[4], u[2];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float keep = b5 ? x[8 + j] : x[j];
+    const float send = b5 ? x[j] : x[8 + j];
+    y[j] = keep + __shfl_xor(send, 32);
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float keep = b4 ? y[4 + j] : y[j];
+    const float send = b4 ? y[j] : y[4 + j];
+    z[j] = keep + __shfl_xor(send, 16);
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const float keep = b3 ? z[2 + j] : z[j];
+    const float send = b3 ? z[j] : z[2 + j];
+    u[j] = keep + __shfl_xor(send, 8);
+  }
+  float s = (b2 ? u[1] : u[0]) + __shfl_xor(b2 ? u[0] : u[1], 4);
+  s += __shfl_xor(s, 2);
+  s += __shfl_xor(s, 1);
+  return s;
+}
+
+__device__ __forceinline__ int lane_of_sum(int v) {
+  return ((v >> 3) & 1) * 32 + ((v >> 2) & 1) * 16 + ((v >> 1) & 1) * 8 + (v & 1) * 4;
 }
 
 template <int REF>
-__global__ __launch_bounds__(kThreadsPrep, 2) void prep_kernel(Plan p) {
-  extern __shared__ __attribute__((aligned(16))) char lds[];
-  float* Gs = reinterpret_cast<float*>(lds + kOffG);
+__device__ void process_item(const Plan& p, const Item& it, const Inputs& in, char* lds, int w, int lane) {
+  constexpr int NB = 32 / REF;
+  constexpr int OX = off_x(REF);
+  float* tot = reinterpret_cast<float*>(lds + kOffTot);
   float* betas = reinterpret_cast<float*>(lds + kOffBeta);
   float* As = reinterpret_cast<float*>(lds + kOffA);
   float* Ps = reinterpret_cast<float*>(lds + kOffP);
-
-  const int cid = blockIdx.x;
-  const int h = blockIdx.y;
+  float* Ts = reinterpret_cast<float*>(lds + kOffT);
+  float* Ms = reinterpret_cast<float*>(lds + kOffM);
+  float* Gref = reinterpret_cast<float*>(lds + kOffGref);
+  char* X = lds + OX;
   const int tid = threadIdx.x;
-  const int H = p.H;
-  const int seq = p.d_table[2 * cid];
-  const int jc = p.d_table[2 * cid + 1];
-  const int t0 = p.d_cu[seq] + kChunk * jc;
-  const int len = min(kChunk, p.d_cu[seq + 1] - t0);
-  char* rec = reinterpret_cast<char*>(p.ws) + ((size_t)h * p.n_chunks + cid) * kRecBytes;
+  const int c0 = 2 * lane;
+  const int len = it.len;
+  char* rec = reinterpret_cast<char*>(p.ws) + ((size_t)it.h * p.n_chunks + it.cid) * kRecBytes;
 
-  // ---------------------------------------------------------------- elementwise phase
-  // Thread (r, cg): row r of the chunk, key/value channels c0 .. c0 + 15.
-  const int r = tid >> 3;
-  const int c0 = (tid & 7) * 16;
-  const bool valid = r < len;
-  float qn[16], kn[16], vv[16], G[16];
-  float beta = 0.f;
+  // ---------------------------------------------------------------- elementwise
+  float qn[8][2], kn[8][2], G[8][2];
   {
-    float gr[16];
-    if (valid) {
-      const size_t base = ((size_t)(t0 + r) * H + h) * kHead + c0;
-      load_bf16x16(p.q, base, qn);
-      load_bf16x16(p.k, base, kn);
-      load_bf16x16(p.v, base, vv);
-      if (p.g_dtype == kF32) {
-        const float4* gp = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(p.g_raw) + base);
+    float sq[16];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float4 t = gp[i];
-          gr[4 * i] = t.x; gr[4 * i + 1] = t.y; gr[4 * i + 2] = t.z; gr[4 * i + 3] = t.w;
-        }
-      } else {
-        load_bf16x16(p.g_raw, base, gr);
-      }
-      const size_t bidx = (size_t)(t0 + r) * H + h;
-      const float braw = (p.beta_dtype == kF32)
-                             ? reinterpret_cast<const float*>(p.beta_raw)[bidx]
-                             : bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(p.beta_raw)[bidx]);
-      beta = sigmoidf_fast(braw);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) { qn[i] = 0.f; kn[i] = 0.f; vv[i] = 0.f; }
+    for (int i = 0; i < 8; ++i) {
+      const bool valid = 8 * w + i < len;
+      qn[i][0] = valid ? lo16(in.q[i]) : 0.f;
+      qn[i][1] = valid ? hi16(in.q[i]) : 0.f;
+      kn[i][0] = valid ? lo16(in.k[i]) : 0.f;
+      kn[i][1] = valid ? hi16(in.k[i]) : 0.f;
+      sq[i] = qn[i][0] * qn[i][0] + qn[i][1] * qn[i][1];
+      sq[8 + i] = kn[i][0] * kn[i][0] + kn[i][1] * kn[i][1];
     }
-    // q/k L2 normalisation over the 128 channels (8 lanes per row).
-    float sq = 0.f, sk = 0.f;
+    const float s = wave_sum16(sq, lane);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) { sq = fmaf(qn[i], qn[i], sq); sk = fmaf(kn[i], kn[i], sk); }
-#pragma unroll
-    for (int off = 1; off < 8; off <<= 1) {
-      sq += __shfl_xor(sq, off);
-      sk += __shfl_xor(sk, off);
+    for (int i = 0; i < 8; ++i) {
+      const float rq = rsqrtf(__shfl(s, lane_of_sum(i)) + 1e-6f);
+      const float rk = rsqrtf(__shfl(s, lane_of_sum(8 + i)) + 1e-6f);
+      qn[i][0] *= rq; qn[i][1] *= rq;
+      kn[i][0] *= rk; kn[i][1] *= rk;
     }
-    const float rq = rsqrtf(sq + 1e-6f), rk = rsqrtf(sk + 1e-6f);
+    // Gate per key channel and its cumsum over this wave's rows (padding rows: g = 0).
+    float run0 = 0.f, run1 = 0.f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) { qn[i] *= rq; kn[i] *= rk; }
-    // Gate per key channel; padding rows contribute g = 0.
-    float4* grow = reinterpret_cast<float4*>(Gs + r * kHead + c0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float4 t;
-      t.x = valid ? p.lower_bound * sigmoidf_fast(gr[4 * i]) : 0.f;
-      t.y = valid ? p.lower_bound * sigmoidf_fast(gr[4 * i + 1]) : 0.f;
-      t.z = valid ? p.lower_bound * sigmoidf_fast(gr[4 * i + 2]) : 0.f;
-      t.w = valid ? p.lower_bound * sigmoidf_fast(gr[4 * i + 3]) : 0.f;
-      grow[i] = t;
+    for (int i = 0; i < 8; ++i) {
+      const bool valid = 8 * w + i < len;
+      run0 += valid ? p.lower_bound * sigm(in.g[i].x) : 0.f;
+      run1 += valid ? p.lower_bound * sigm(in.g[i].y) : 0.f;
+      G[i][0] = run0;
+      G[i][1] = run1;
     }
-    if ((tid & 7) == 0) betas[r] = beta;  // 0 on padding rows
-  }
-  // Zero the A / P tiles (the block above the diagonal is never written).
-  for (int i = tid; i < 2 * 32 * LDS_F; i += kThreadsPrep) As[i] = 0.f;  // As and Ps are adjacent
-  __syncthreads();
-
-  // In-chunk inclusive cumsum, one thread per key channel, rows in order.
-  if (tid < kHead) {
-    float acc = 0.f;
-#pragma unroll 8
-    for (int rr = 0; rr < kChunk; ++rr) {
-      acc += Gs[rr * kHead + tid];
-      Gs[rr * kHead + tid] = acc;
-    }
+    *reinterpret_cast<float2*>(tot + w * 128 + c0) = make_float2(run0, run1);
+    if (lane < 8) betas[8 * w + lane] = (8 * w + lane < len) ? sigm(in.braw) : 0.f;
   }
   __syncthreads();
+  {
+    // Add the totals of the earlier waves (in wave order), then publish reference rows.
+    float o0 = 0.f, o1 = 0.f;
+    for (int ww = 0; ww < w; ++ww) {
+      const float2 t = *reinterpret_cast<const float2*>(tot + ww * 128 + c0);
+      o0 += t.x;
+      o1 += t.y;
+    }
 #pragma unroll
-  for (int i = 0; i < 16; ++i) G[i] = Gs[r * kHead + c0 + i];
+    for (int i = 0; i < 8; ++i) {
+      G[i][0] += o0;
+      G[i][1] += o1;
+      const int r = 8 * w + i;
+      if (r % REF == 0) *reinterpret_cast<float2*>(Gref + (r / REF) * 128 + c0) = make_float2(G[i][0], G[i][1]);
+    }
+    if (w == 3) *reinterpret_cast<float2*>(Gref + NB * 128 + c0) = make_float2(G[7][0], G[7][1]);  // G_C
+  }
+  __syncthreads();
 
   // ---------------------------------------------------------------- A and P on MFMA
   {
-    const int m = (r / REF) * REF;
-    __bf16 lkh[16], lkl[16], lqh[16], lql[16];
+    __bf16 lkh[8][2], lkl[8][2], lqh[8][2], lql[8][2];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float e = __expf(G[i] - Gs[m * kHead + c0 + i]);  // in [e^-80, 1]
-      split_bf16(kn[i] * e, lkh[i], lkl[i]);
-      split_bf16(qn[i] * e, lqh[i], lql[i]);
+    for (int i = 0; i < 8; ++i) {
+      const int r = 8 * w + i;
+      const float2 gm = *reinterpret_cast<const float2*>(Gref + (r / REF) * 128 + c0);
+      const float e0 = __expf(G[i][0] - gm.x), e1 = __expf(G[i][1] - gm.y);  // in [e^-80, 1]
+      split_bf16(kn[i][0] * e0, lkh[i][0], lkl[i][0]);
+      split_bf16(kn[i][1] * e1, lkh[i][1], lkl[i][1]);
+      split_bf16(qn[i][0] * e0, lqh[i][0], lql[i][0]);
+      split_bf16(qn[i][1] * e1, lqh[i][1], lql[i][1]);
+      const int o = (r * LDA + c0) * 2;
+      *reinterpret_cast<uint32_t*>(X + xLKh + o) = pack2(lkh[i][0], lkh[i][1]);
+      *reinterpret_cast<uint32_t*>(X + xLKl + o) = pack2(lkl[i][0], lkl[i][1]);
+      *reinterpret_cast<uint32_t*>(X + xLQh + o) = pack2(lqh[i][0], lqh[i][1]);
+      *reinterpret_cast<uint32_t*>(X + xLQl + o) = pack2(lql[i][0], lql[i][1]);
     }
-    const int o = (r * LDA + c0) * 2;
-    st_row16(lds, kOffLKh + o, lkh);
-    st_row16(lds, kOffLKl + o, lkl);
-    st_row16(lds, kOffLQh + o, lqh);
-    st_row16(lds, kOffLQl + o, lql);
   }
-
-  const int w = tid >> 6, lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
+  const int l16 = lane & 15, g4 = lane >> 4;
   // Tile jobs per wave: (row tile, column tile, matrix A=0 / P=1).
   //   wave 0: (0,0,A) (0,0,P); wave 1: (1,0,A) (1,0,P); wave 2: (1,1,A); wave 3: (1,1,P)
   const int njobs = (w < 2) ? 2 : 1;
-  int jt[2], ja[2], jm[2];
-  if (w < 2) { jt[0] = w; ja[0] = 0; jm[0] = 0; jt[1] = w; ja[1] = 0; jm[1] = 1; }
-  else { jt[0] = 1; ja[0] = 1; jm[0] = w - 2; jt[1] = 1; ja[1] = 1; jm[1] = w - 2; }
+  const int jt = (w < 2) ? w : 1;
+  const int ja = (w < 2) ? 0 : 1;
   f32x4 acc[2] = {zero4(), zero4()};
-
-  for (int b = 0; b < kChunk / REF; ++b) {
+  for (int b = 0; b < NB; ++b) {
     const int mb = b * REF;
     const int lim = mb + REF - 1;  // last row of the block: right factors beyond it are 0
     {
-      __bf16 rh[16], rl[16];
+      const float2 gm = *reinterpret_cast<const float2*>(Gref + b * 128 + c0);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float x = 0.f;
-        if (r <= lim) x = kn[i] * __expf(Gs[mb * kHead + c0 + i] - G[i]);  // <= e^80
-        split_bf16(x, rh[i], rl[i]);
+      for (int i = 0; i < 8; ++i) {
+        const int r = 8 * w + i;
+        float x0 = 0.f, x1 = 0.f;
+        if (r <= lim) {
+          x0 = kn[i][0] * __expf(gm.x - G[i][0]);  // <= e^80
+          x1 = kn[i][1] * __expf(gm.y - G[i][1]);
+        }
+        __bf16 h0, l0, h1, l1;
+        split_bf16(x0, h0, l0);
+        split_bf16(x1, h1, l1);
+        const int o = (r * LDA + c0) * 2;
+        *reinterpret_cast<uint32_t*>(X + xRh + o) = pack2(h0, h1);
+        *reinterpret_cast<uint32_t*>(X + xRl + o) = pack2(l0, l1);
       }
-      const int o = (r * LDA + c0) * 2;
-      st_row16(lds, kOffRh + o, rh);
-      st_row16(lds, kOffRl + o, rl);
     }
     __syncthreads();
-#pragma unroll
-    for (int jb = 0; jb < 2; ++jb) {
-      if (jb >= njobs) break;
-      const int t = jt[jb], a = ja[jb];
-      if (mb < 16 * t || mb >= 16 * t + 16 || 16 * a > lim) continue;
-      const int row = 16 * t + l16;
+    if (mb >= 16 * jt && mb < 16 * jt + 16 && 16 * ja <= lim) {
+      const int row = 16 * jt + l16;
       const bool rowin = (row >= mb) && (row <= lim);
-      const int offLh = jm[jb] ? kOffLQh : kOffLKh;
-      const int offLl = jm[jb] ? kOffLQl : kOffLKl;
-      const int col = 16 * a + l16;
+      const int col = 16 * ja + l16;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         const int ea = (row * LDA + 32 * kk + 8 * g4) * 2;
         const int eb = (col * LDA + 32 * kk + 8 * g4) * 2;
-        bf16x8 ah = ld_frag(lds, offLh + ea), al = ld_frag(lds, offLl + ea);
-        if (!rowin) { ah = bf16x8{}; al = bf16x8{}; }
-        const bf16x8 bh = ld_frag(lds, kOffRh + eb), bl = ld_frag(lds, kOffRl + eb);
-        acc[jb] = mfma(ah, bh, acc[jb]);
-        acc[jb] = mfma(ah, bl, acc[jb]);
-        acc[jb] = mfma(al, bh, acc[jb]);
+        const bf16x8 bh = ld_frag(X, xRh + eb), bl = ld_frag(X, xRl + eb);
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb) {
+          if (jb >= njobs) break;
+          const int mat = (w < 2) ? jb : (w - 2);
+          bf16x8 ah = ld_frag(X, (mat ? xLQh : xLKh) + ea), al = ld_frag(X, (mat ? xLQl : xLKl) + ea);
+          if (!rowin) { ah = bf16x8{}; al = bf16x8{}; }
+          acc[jb] = mfma(ah, bh, acc[jb]);
+          acc[jb] = mfma(ah, bl, acc[jb]);
+          acc[jb] = mfma(al, bh, acc[jb]);
+        }
       }
     }
     __syncthreads();
   }
-  // Masked, scaled tiles into LDS: A strictly lower times beta_r, P lower with diagonal.
+  // Masked, scaled tiles: A strictly lower times beta_r, P lower with diagonal. The tile
+  // above the diagonal is written as zeros.
+  {
+    const int col = 16 * ja + l16;
 #pragma unroll
-  for (int jb = 0; jb < 2; ++jb) {
-    if (jb >= njobs) break;
-    const int t = jt[jb], a = ja[jb];
-    const int col = 16 * a + l16;
+    for (int jb = 0; jb < 2; ++jb) {
+      if (jb >= njobs) break;
+      const int mat = (w < 2) ? jb : (w - 2);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = 16 * t + 4 * g4 + i;
-      if (jm[jb] == 0) As[row * LDS_F + col] = (col < row) ? betas[row] * acc[jb][i] : 0.f;
-      else Ps[row * LDS_F + col] = (col <= row) ? p.scale * acc[jb][i] : 0.f;
+      for (int i = 0; i < 4; ++i) {
+        const int row = 16 * jt + 4 * g4 + i;
+        if (mat == 0) As[row * LDF + col] = (col < row) ? betas[row] * acc[jb][i] : 0.f;
+        else Ps[row * LDF + col] = (col <= row) ? p.scale * acc[jb][i] : 0.f;
+      }
+    }
+    if (w >= 2) {  // upper tile (0,1) of A (wave 2) and of P (wave 3)
+      float* dst = (w == 2) ? As : Ps;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[(4 * g4 + i) * LDF + 16 + l16] = 0.f;
     }
   }
 
-  // ---------------------------------------------------------------- staging for products
+  // ---------------------------------------------------------------- staging
   // (the factor tiles are dead after the last barrier of the loop above)
   {
-    __bf16 kgh[16], kgl[16], qs[16];
-    __bf16* KGh = reinterpret_cast<__bf16*>(lds + kOffKGh);
-    __bf16* KGl = reinterpret_cast<__bf16*>(lds + kOffKGl);
-    __bf16* Kt = reinterpret_cast<__bf16*>(lds + kOffKt);
-    __bf16* Vt = reinterpret_cast<__bf16*>(lds + kOffVt);
+    const float2 gc = *reinterpret_cast<const float2*>(Gref + NB * 128 + c0);
+    __bf16 kg0h[8], kg0l[8], kg1h[8], kg1l[8], kt0[8], kt1[8], v0[8], v1[8];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float eg = __expf(G[i]);                               // e^{G_r} <= 1
-      const float ec = __expf(Gs[31 * kHead + c0 + i] - G[i]);     // e^{G_C - G_r} <= 1
-      split_bf16(kn[i] * eg, kgh[i], kgl[i]);
-      qs[i] = to_bf16(p.scale * qn[i] * eg);
-      const int c = c0 + i;
-      KGh[c * LDT + r] = kgh[i];
-      KGl[c * LDT + r] = kgl[i];
-      Kt[c * LDT + r] = to_bf16(kn[i] * ec);
-      Vt[c * LDT + r] = to_bf16(vv[i]);  // exact: v is bf16
+    for (int i = 0; i < 8; ++i) {
+      const int r = 8 * w + i;
+      const float eg0 = __expf(G[i][0]), eg1 = __expf(G[i][1]);            // e^{G_r} <= 1
+      const float ec0 = __expf(gc.x - G[i][0]), ec1 = __expf(gc.y - G[i][1]);  // e^{G_C - G_r} <= 1
+      split_bf16(kn[i][0] * eg0, kg0h[i], kg0l[i]);
+      split_bf16(kn[i][1] * eg1, kg1h[i], kg1l[i]);
+      kt0[i] = to_bf16(kn[i][0] * ec0);
+      kt1[i] = to_bf16(kn[i][1] * ec1);
+      const bool valid = r < len;
+      v0[i] = valid ? __builtin_bit_cast(__bf16, (uint16_t)(in.v[i] & 0xffffu)) : to_bf16(0.f);
+      v1[i] = valid ? __builtin_bit_cast(__bf16, (uint16_t)(in.v[i] >> 16)) : to_bf16(0.f);
+      *reinterpret_cast<uint32_t*>(X + xQs + (r * LDA + c0) * 2) =
+          pack2(to_bf16(p.scale * qn[i][0] * eg0), to_bf16(p.scale * qn[i][1] * eg1));
     }
-    st_row16(lds, kOffQs + (r * LDA + c0) * 2, qs);
-    if (r == 0) {
-      float4* E = reinterpret_cast<float4*>(rec + kRecE + c0 * 4);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float4 e;
-        e.x = __expf(Gs[31 * kHead + c0 + 4 * i]);
-        e.y = __expf(Gs[31 * kHead + c0 + 4 * i + 1]);
-        e.z = __expf(Gs[31 * kHead + c0 + 4 * i + 2]);
-        e.w = __expf(Gs[31 * kHead + c0 + 4 * i + 3]);
-        E[i] = e;
-      }
-    }
+    st_col8(X, xKGh, c0, w, kg0h);
+    st_col8(X, xKGh, c0 + 1, w, kg1h);
+    st_col8(X, xKGl, c0, w, kg0l);
+    st_col8(X, xKGl, c0 + 1, w, kg1l);
+    st_col8(X, xKt, c0, w, kt0);
+    st_col8(X, xKt, c0 + 1, w, kt1);
+    st_col8(X, xVt, c0, w, v0);
+    st_col8(X, xVt, c0 + 1, w, v1);
+    if (w == 3) *reinterpret_cast<float2*>(rec + kRecE + c0 * 4) = make_float2(__expf(gc.x), __expf(gc.y));
   }
   __syncthreads();
 
-  // ---------------------------------------------------------------- solve + fragment stores
+  // ---------------------------------------------------------------- solve (part 1) + stores
   if (w == 0) {
     if (lane < 32) {
-      // Column j = lane of T = (I + A)^{-1}: T[i][j] = [i == j] - sum_{p < i} A[i][p] T[p][j].
-      const int j = lane;
-      float tc[32];
+      // Diagonal 16x16 blocks of T = (I + A)^{-1}: lane -> (block, column j). Forward
+      // substitution T[i][j] = [i == j] - sum_{j <= k < i} A[i][k] T[k][j], with the sum
+      // split over four accumulators to shorten the dependent chain.
+      const int blk = lane >> 4, j = lane & 15, base = 16 * blk;
+      float tc[16];
 #pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        float s = (i == j) ? 1.f : 0.f;
-        const float* Ai = As + i * LDS_F;
+      for (int i = 0; i < 16; ++i) {
+        const float* Ai = As + (base + i) * LDF + base;
+        float s0 = (i == j) ? 1.f : 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
 #pragma unroll
-        for (int q4 = 0; q4 < i; ++q4) s = fmaf(-Ai[q4], tc[q4], s);
-        tc[i] = s;
+        for (int k = 0; k < i; k += 4) {
+          s0 = fmaf(-Ai[k], tc[k], s0);
+          if (k + 1 < i) s1 = fmaf(-Ai[k + 1], tc[k + 1], s1);
+          if (k + 2 < i) s2 = fmaf(-Ai[k + 2], tc[k + 2], s2);
+          if (k + 3 < i) s3 = fmaf(-Ai[k + 3], tc[k + 3], s3);
+        }
+        tc[i] = (s0 + s1) + (s2 + s3);
       }
-      const float bj = betas[j];
-      __bf16* Th = reinterpret_cast<__bf16*>(lds + kOffTh);
-      __bf16* Tl = reinterpret_cast<__bf16*>(lds + kOffTl);
 #pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        __bf16 hi, lo;
-        split_bf16(tc[i] * bj, hi, lo);  // T diag(beta)
-        Th[i * LDT + j] = hi;
-        Tl[i * LDT + j] = lo;
-      }
+      for (int i = 0; i < 16; ++i) Ts[(base + i) * LDF + base + j] = tc[i];
     }
   } else {
     // 18 fragments (Q: 8, K: 8, P: 2), six per wave.
@@ -333,24 +407,56 @@ __global__ __launch_bounds__(kThreadsPrep, 2) void prep_kernel(Plan p) {
       if (f < 8) {
         const int t = f >> 2, m = f & 3;
         const int row = 16 * t + l16;
-        const int o0 = kOffQs + (row * LDA + 32 * m + 4 * g4) * 2;
-        val = ld_frag_2x4(lds, o0, o0 + 32);
+        const int o0 = xQs + (row * LDA + 32 * m + 4 * g4) * 2;
+        val = ld_frag_2x4(X, o0, o0 + 32);
         dst = kRecQ + (size_t)f * kFrag;
       } else if (f < 16) {
         const int kt = f - 8;
         const int krow = 16 * kt + l16;
-        const int o0 = kOffKt + (krow * LDT + 4 * g4) * 2;
-        val = ld_frag_2x4(lds, o0, o0 + 32);
+        const int o0 = xKt + (krow * LDT + 4 * g4) * 2;
+        val = ld_frag_2x4(X, o0, o0 + 32);
         dst = kRecK + (size_t)kt * kFrag;
       } else {
         const int t = f - 16;
-        const float* Pr = Ps + (16 * t + l16) * LDS_F;
-        f32x4 a = {Pr[4 * g4], Pr[4 * g4 + 1], Pr[4 * g4 + 2], Pr[4 * g4 + 3]};
-        f32x4 b = {Pr[16 + 4 * g4], Pr[16 + 4 * g4 + 1], Pr[16 + 4 * g4 + 2], Pr[16 + 4 * g4 + 3]};
+        const float* Pr = Ps + (16 * t + l16) * LDF;
+        const f32x4 a = {Pr[4 * g4], Pr[4 * g4 + 1], Pr[4 * g4 + 2], Pr[4 * g4 + 3]};
+        const f32x4 b = {Pr[16 + 4 * g4], Pr[16 + 4 * g4 + 1], Pr[16 + 4 * g4 + 2], Pr[16 + 4 * g4 + 3]};
         val = pack8(a, b);
         dst = kRecP + (size_t)t * kFrag;
       }
       *reinterpret_cast<bf16x8*>(rec + dst + lane * 16) = val;
+    }
+  }
+  __syncthreads();
+  // ---------------------------------------------------------------- solve (part 2)
+  // Off-diagonal block: T10 = -T11 A10 T00, one 16x16 output element per thread.
+  {
+    const int i = tid >> 4, j = tid & 15;
+    float m = 0.f;
+    for (int k = j; k < 16; ++k) m = fmaf(As[(16 + i) * LDF + k], Ts[k * LDF + j], m);  // (A10 T00)[i][j]
+    Ms[i * LDF + j] = m;
+  }
+  __syncthreads();
+  {
+    const int i = tid >> 4, j = tid & 15;
+    float t = 0.f;
+    for (int k = 0; k <= i; ++k) t = fmaf(Ts[(16 + i) * LDF + 16 + k], Ms[k * LDF + j], t);
+    Ts[(16 + i) * LDF + j] = -t;
+  }
+  __syncthreads();
+  // T diag(beta) as hi/lo bf16 (rows r, column r'), zero above the diagonal.
+  {
+    __bf16* Th = reinterpret_cast<__bf16*>(X + xTh);
+    __bf16* Tl = reinterpret_cast<__bf16*>(X + xTl);
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int e = tid + 256 * q4;
+      const int i = e >> 5, j = e & 31;
+      const float x = (j <= i) ? Ts[i * LDF + j] * betas[j] : 0.f;
+      __bf16 hi, lo;
+      split_bf16(x, hi, lo);
+      Th[i * LDT + j] = hi;
+      Tl[i * LDT + j] = lo;
     }
   }
   __syncthreads();
@@ -362,52 +468,79 @@ __global__ __launch_bounds__(kThreadsPrep, 2) void prep_kernel(Plan p) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const int rrow = 16 * t + l16;
-      const bf16x8 th = ld_frag(lds, kOffTh + (rrow * LDT + 8 * g4) * 2);
-      const bf16x8 tl = ld_frag(lds, kOffTl + (rrow * LDT + 8 * g4) * 2);
+      const bf16x8 th = ld_frag(X, xTh + (rrow * LDT + 8 * g4) * 2);
+      const bf16x8 tl = ld_frag(X, xTl + (rrow * LDT + 8 * g4) * 2);
 #pragma unroll
       for (int q2 = 0; q2 < 2; ++q2) {
         const int ct = 2 * w + q2;
         const int crow = 16 * ct + l16;
         // W^T tile (ct, t) = (k e^G)^T (T diag beta)^T: A = KG^T rows c, B = T' rows r.
-        const bf16x8 kh = ld_frag(lds, kOffKGh + (crow * LDT + 8 * g4) * 2);
-        const bf16x8 kl = ld_frag(lds, kOffKGl + (crow * LDT + 8 * g4) * 2);
+        const bf16x8 kh = ld_frag(X, xKGh + (crow * LDT + 8 * g4) * 2);
+        const bf16x8 kl = ld_frag(X, xKGl + (crow * LDT + 8 * g4) * 2);
         f32x4 a = zero4();
         a = mfma(kh, th, a);
         a = mfma(kh, tl, a);
         a = mfma(kl, th, a);
         dw[t][q2] = a;
         // U tile (t, ct) = T' v: A = T' rows r, B = v columns.
-        const bf16x8 vt = ld_frag(lds, kOffVt + (crow * LDT + 8 * g4) * 2);
-        f32x4 u = zero4();
-        u = mfma(th, vt, u);
-        u = mfma(tl, vt, u);
-        du[t][q2] = u;
+        const bf16x8 vt = ld_frag(X, xVt + (crow * LDT + 8 * g4) * 2);
+        f32x4 uu = zero4();
+        uu = mfma(th, vt, uu);
+        uu = mfma(tl, vt, uu);
+        du[t][q2] = uu;
       }
     }
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const bf16x8 fw = pack8(dw[t][0], dw[t][1]);
-      *reinterpret_cast<bf16x8*>(rec + kRecW + (size_t)(t * 4 + w) * kFrag + lane * 16) = fw;
-    }
+    for (int t = 0; t < 2; ++t)
+      *reinterpret_cast<bf16x8*>(rec + kRecW + (size_t)(t * 4 + w) * kFrag + lane * 16) = pack8(dw[t][0], dw[t][1]);
 #pragma unroll
-    for (int q2 = 0; q2 < 2; ++q2) {
-      const bf16x8 fu = pack8(du[0][q2], du[1][q2]);
-      *reinterpret_cast<bf16x8*>(rec + kRecU + (size_t)(2 * w + q2) * kFrag + lane * 16) = fu;
-    }
+    for (int q2 = 0; q2 < 2; ++q2)
+      *reinterpret_cast<bf16x8*>(rec + kRecU + (size_t)(2 * w + q2) * kFrag + lane * 16) = pack8(du[0][q2], du[1][q2]);
   }
 }
 
 template <int REF>
-int launch_ref(const Plan& p, hipStream_t s) {
+__global__ __launch_bounds__(kThreadsPrep, 2) void prep_kernel(Plan p, int n_items) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (blockIdx.x == 0) {
+    // Fresh progress counters for the scan's L2 prefetchers (a hint only).
+    for (int u = threadIdx.x; u < p.N * p.H; u += kThreadsPrep) p.progress[u] = 0u;
+  }
+  const int step = gridDim.x;
+  int item = blockIdx.x;
+  if (item >= n_items) return;
+  // Two input buffers; the next item's loads are unconditional (clamped) so the wait
+  // before each item covers only its own inputs.
+  Inputs ia, ib;
+  Item ta = item_of(p, item), tb;
+  load_inputs(p, ta, w, lane, ia);
+  for (;;) {
+    tb = item_of(p, min(item + step, n_items - 1));
+    load_inputs(p, tb, w, lane, ib);
+    process_item<REF>(p, ta, ia, lds, w, lane);
+    item += step;
+    if (item >= n_items) break;
+    ta = item_of(p, min(item + step, n_items - 1));
+    load_inputs(p, ta, w, lane, ia);
+    process_item<REF>(p, tb, ib, lds, w, lane);
+    item += step;
+    if (item >= n_items) break;
+  }
+}
+
+template <int REF>
+int launch_ref(const Plan& p, hipStream_t s, int grid) {
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prep_kernel<REF>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes(REF));
     if (e != hipSuccess) return (int)e;
     attr_set = true;
   }
-  dim3 grid(p.n_chunks, p.H);
-  hipLaunchKernelGGL(prep_kernel<REF>, grid, dim3(kThreadsPrep), kLdsBytes, s, p);
+  const int n_items = p.n_chunks * p.H;
+  hipLaunchKernelGGL(prep_kernel<REF>, dim3(min(grid, n_items)), dim3(kThreadsPrep), lds_bytes(REF), s, p, n_items);
   return (int)hipGetLastError();
 }
 
@@ -416,12 +549,13 @@ int launch_ref(const Plan& p, hipStream_t s) {
 int launch_prep(const Plan& p, void* stream) {
   if (p.n_chunks == 0) return 0;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int grid = 2 * p.cu_count;  // persistent: two resident workgroups per CU
   switch (p.ref_block) {
-    case 16: return launch_ref<16>(p, s);
-    case 8: return launch_ref<8>(p, s);
-    case 4: return launch_ref<4>(p, s);
-    case 2: return launch_ref<2>(p, s);
-    default: return launch_ref<1>(p, s);
+    case 16: return launch_ref<16>(p, s, grid);
+    case 8: return launch_ref<8>(p, s, grid);
+    case 4: return launch_ref<4>(p, s, grid);
+    case 2: return launch_ref<2>(p, s, grid);
+    default: return launch_ref<1>(p, s, grid);
   }
 }
 
