@@ -190,8 +190,6 @@ struct ProfileMarks {
 struct kda_ctx {
   kda_runtime rt{};
   int dv_split_override = 0;  // tuning only (KDA_DV_SPLIT), 0 = policy
-  int prefetchers = 0;        // tuning only (KDA_PREFETCH); off: measured slower
-  int prefetch_ahead = 16;    // tuning only (KDA_PREFETCH_AHEAD)
   bool profiling = false;
   std::vector<ProfileMarks> marks;       // recorded, not yet read
   std::vector<ProfileMarks> marks_free;  // reusable
@@ -413,7 +411,7 @@ size_t kda_chunk_fwd_workspace_bytes(const kda_fwd_args* a) {
   if (kda_chunk_fwd_validate(a) != KDA_OK) return 0;
   // Chunks over all sequences are at most ceil(T / 32) + N (one partial chunk each).
   const int64_t max_chunks = ((int64_t)a->T + kChunk - 1) / kChunk + a->N;
-  return kda::progress_bytes((int64_t)a->N * a->H) + (size_t)a->H * (size_t)max_chunks * kda::kRecBytes;
+  return (size_t)a->H * (size_t)max_chunks * kda::kRecBytes;
 }
 
 kda_status kda_prepare_chunk_indices(const int32_t* cu_host, int32_t n_seqs, int32_t chunk, int32_t* pairs_out,
@@ -449,8 +447,6 @@ kda_status kda_ctx_create_with_runtime(const kda_runtime* rt, int cu_count, kda_
     const int v = std::atoi(e);
     if (v == 2 || v == 4 || v == 8) ctx->dv_split_override = v;
   }
-  if (const char* e = std::getenv("KDA_PREFETCH")) ctx->prefetchers = std::max(0, std::min(8, std::atoi(e)));
-  if (const char* e = std::getenv("KDA_PREFETCH_AHEAD")) ctx->prefetch_ahead = std::max(1, std::min(256, std::atoi(e)));
   ctx->ring.resize(kRingSlots);
   *out = ctx;
   return KDA_OK;
@@ -581,15 +577,8 @@ kda_status kda_chunk_fwd(kda_ctx* ctx, const kda_fwd_args* a, void* ws, size_t w
   p.indices = a->state_indices;
   p.flags = a->has_initial_state;
   p.out = a->out;
-  const int64_t units = (int64_t)a->N * a->H;
-  p.progress = reinterpret_cast<uint32_t*>(ws);
-  p.ws = reinterpret_cast<char*>(ws) + kda::progress_bytes(units);
-  // L2 prefetch workgroups only pay while the scan leaves most CUs idle.
-  p.prefetchers = 0;
-  p.prefetch_ahead = ctx->prefetch_ahead;
+  p.ws = ws;
   p.cu_count = ctx->cu_count;
-  if (ctx->prefetchers > 0 && units * (p.dv_split + ctx->prefetchers) <= 2 * (int64_t)ctx->cu_count)
-    p.prefetchers = ctx->prefetchers;
 
   ProfileMarks pm{};
   if (ctx->profiling) {

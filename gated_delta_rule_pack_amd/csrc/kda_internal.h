@@ -10,7 +10,7 @@ namespace kda {
 constexpr int kChunk = 32;    // tokens per chunk
 constexpr int kHead = 128;    // K = V = 128
 constexpr int kThreadsPrep = 256;
-constexpr int kThreadsScan = 128;
+constexpr int kThreadsScan = 256;
 
 // Per (head, chunk) workspace record written by prep and read by scan. Every tile is
 // stored in the exact per-lane order the scan's MFMA operands use, so the scan issues
@@ -59,14 +59,8 @@ struct Plan {
   const uint8_t* flags;
   void* out;
   void* ws;             // first chunk record (256-byte aligned)
-  uint32_t* progress;   // [N*H] chunks finished per (sequence, head), written by the scan
-  int prefetchers;      // L2 prefetch workgroups per (sequence, head); 0 = none
-  int prefetch_ahead;   // how many chunks ahead of the scan they may run
   int cu_count;         // compute units of the device (persistent grid sizing)
 };
-
-// Workspace: [progress counters, padded to 256 bytes][records].
-inline size_t progress_bytes(int64_t units) { return (size_t)((units * 4 + 255) / 256 * 256); }
 
 // Launchers (defined in the .hip files). Return 0 on success, nonzero HIP error code.
 int launch_prep(const Plan& p, void* stream);

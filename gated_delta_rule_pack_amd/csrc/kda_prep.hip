@@ -504,10 +504,6 @@ __global__ __launch_bounds__(kThreadsPrep, 2) void prep_kernel(Plan p, int n_ite
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  if (blockIdx.x == 0) {
-    // Fresh progress counters for the scan's L2 prefetchers (a hint only).
-    for (int u = threadIdx.x; u < p.N * p.H; u += kThreadsPrep) p.progress[u] = 0u;
-  }
   const int step = gridDim.x;
   int item = blockIdx.x;
   if (item >= n_items) return;

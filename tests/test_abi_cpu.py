@@ -149,8 +149,7 @@ def test_workspace_bytes(lib):
         a, _, _ = _valid_args(bufs, T=T, N=N, H=H, cu=cu)
         if T == 0:
             a.q = a.k = a.v = a.g_raw = a.beta_raw = a.out = None
-        header = (4 * N * H + 255) // 256 * 256  # per (sequence, head) progress counters
-        assert lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(a)) == header + H * ((T + 31) // 32 + N) * REC
+        assert lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(a)) == H * ((T + 31) // 32 + N) * REC
 
 
 # ---------------------------------------------------------------- chunk table, policies
