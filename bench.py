@@ -29,10 +29,10 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
 RECORD_BYTES = 35328  # per (head, chunk) workspace record written by prep, read by scan
 
 WORKLOADS = {
-    "cfg2": (2, "1x4096 tokens, H=12, K=V=128, paged fp32 state pool [64,12,128,128]"),
-    "cfg3": (3, "1x16384 tokens, H=12, K=V=128, paged fp32 pool with stride(0) padded by 4096"),
-    "cfg4": (4, "128 varlen sequences (0..2048 tokens, 4 empty), H=12, paged fp32 pool [256,...]"),
-    "cfg5": (5, "256 sequences x 1 token, H=12, paged bf16 pool [512,12,128,128]"),
+    "paged_1x4096_H12": "1x4096 tokens, H=12, K=V=128, paged fp32 state pool [64,12,128,128]",
+    "paged_1x16384_H12_pad": "1x16384 tokens, H=12, K=V=128, paged fp32 pool with stride(0) padded by 4096",
+    "paged_varlen128_H12": "128 varlen sequences (0..2048 tokens, 4 empty), H=12, paged fp32 pool [256,...]",
+    "paged_256x1_H12_bf16": "256 sequences x 1 token, H=12, paged bf16 pool [512,12,128,128]",
 }
 
 
@@ -43,8 +43,11 @@ def _oracle_head(args):
     return kda_forward(q, k, v, g, b, cu, scale=scale, lower_bound=lb, **S)
 
 
-def cpu_baseline(wl, max_tokens: int, workers: int):
-    """Time the fp64 oracle on a bounded sample of the workload (before any GPU use)."""
+def cpu_baseline(wl, max_tokens: int, workers: int, min_seconds: float):
+    """Time the fp64 oracle on a bounded sample of the workload (before any GPU use).
+
+    The sample is repeated until at least ``min_seconds`` of wall time have passed, so a
+    small workload still gives a stable rate."""
     import multiprocessing as mp
 
     import numpy as np
@@ -76,33 +79,42 @@ def cpu_baseline(wl, max_tokens: int, workers: int):
         ctx = mp.get_context("fork")
         with ctx.Pool(workers) as pool:
             pool.map(abs, range(workers))  # start the workers before timing
+            reps = 0
             t0 = time.perf_counter()
-            pool.map(_oracle_head, tasks, chunksize=1)
-            wall = time.perf_counter() - t0
+            while True:
+                pool.map(_oracle_head, tasks, chunksize=1)
+                reps += 1
+                wall = time.perf_counter() - t0
+                if wall >= min_seconds:
+                    break
     tokens = int(cu_s[-1])
     return {
-        "value": tokens / wall, "unit": "tokens/s", "cores": workers, "kind": "oracle",
+        "value": reps * tokens / wall, "unit": "tokens/s", "cores": workers, "kind": "oracle",
         "sample": f"first {tokens} tokens ({take} sequence(s)) of the workload, all {wl.H} heads, "
-                  f"one head per worker process, fp64 numpy token loop",
+                  f"one head per worker process, fp64 numpy token loop, {reps} pass(es)",
         "seconds": wall,
     }
 
 
-def _source_hash(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def kernel_source_hash(kernel: str) -> str:
+    """Hash of the sources one kernel is built from (its .hip file and the shared headers)."""
+    csrc = os.path.join(ROOT, "gated_delta_rule_pack_amd", "csrc")
+    h = hashlib.sha256()
+    for name in (f"kda_{kernel}.hip", "kda_device.h", "kda_internal.h"):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def traffic_from_profiles(kernel: str, workload: str):
     """HBM bytes per launch from the committed counter summary, if its kernel source matches."""
-    path = os.path.join(ROOT, "profiles", f"{kernel}_traffic_{workload}.txt")
-    src = os.path.join(ROOT, "gated_delta_rule_pack_amd", "csrc", f"kda_{kernel}.hip")
+    path = os.path.join(ROOT, "profiles", f"kda_{kernel}_traffic_{workload}.txt")
     if not os.path.exists(path):
         return None
     text = open(path).read()
     m_hash = re.search(r"source_sha256_16:\s*([0-9a-f]+)", text)
     m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not m_hash or not m_bytes or m_hash.group(1) != _source_hash(src):
+    if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash(kernel):
         return None
     return float(m_bytes.group(1))
 
@@ -133,17 +145,46 @@ def algorithmic_bytes(wl, kernel: str, n_chunks: int):
     return th * (3 * 256 + g_b + b_b + 256) + state
 
 
+def copy_calibration(mib: int, steps: int, warmup: int):
+    """Plain device-to-device copies of a known size, for scaling the HBM byte counters."""
+    import torch
+
+    dev = torch.device("cuda", 0)
+    n = mib << 18  # fp32 elements
+    src = torch.rand(n, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    nbytes = n * 4
+    print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "steps": steps,
+                      "us_per_copy": round(ms * 1e3, 2), "GBps": round(2 * nbytes / (ms * 1e-3) / 1e9, 1),
+                      "equal": bool(torch.equal(src, dst))}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="cfg2")
+    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="paged_1x4096_H12")
     ap.add_argument("--rotate", type=int, default=0,
                     help="input sets cycled through (0: enough to exceed the 256 MB MALL)")
     ap.add_argument("--cpu-tokens", type=int, default=4096, help="oracle sample size (tokens)")
     ap.add_argument("--cpu-workers", type=int, default=12)
+    ap.add_argument("--cpu-seconds", type=float, default=2.0, help="minimum oracle wall time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="instead of the workload, run --steps plain device copies of this many MiB "
+                         "(the known-size kernel that scales the HBM byte counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -153,14 +194,18 @@ def main():
               "so per-GPU throughput is the number to read.", file=sys.stderr)
         sys.exit(2)
 
-    from gated_delta_rule_pack_amd.workloads import config
-    cfg_id, cfg_desc = WORKLOADS[args.workload]
-    wl = config(cfg_id)
+    if args.copy_mib:
+        copy_calibration(args.copy_mib, args.steps, args.warmup)
+        return
+
+    from gated_delta_rule_pack_amd.workloads import standard
+    cfg_desc = WORKLOADS[args.workload]
+    wl = standard(args.workload)
 
     # Oracle baseline on the host first, before anything initialises the GPU.
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, args.cpu_tokens, args.cpu_workers)
+        cpu = cpu_baseline(wl, args.cpu_tokens, args.cpu_workers, args.cpu_seconds)
 
     import torch
 
@@ -247,7 +292,7 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
         "us_per_call": round(ms_step * 1e3, 2), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": cfg_desc, "T": wl.T, "N": wl.N, "H": wl.H, "K": 128, "V": 128, "chunk": 32,
+        "config": {"workload": args.workload, "description": cfg_desc, "T": wl.T, "N": wl.N, "H": wl.H, "K": 128, "V": 128, "chunk": 32,
                    "lower_bound": wl.lower_bound, "state": f"{wl.state_mode} {wl.state_dtype}",
                    "dv_split": stats["last_dv_split"], "ref_block": stats["last_ref_block"],
                    "input_sets_rotated": n_rot, "parallelism": "single GPU"},

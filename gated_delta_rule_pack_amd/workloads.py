@@ -173,25 +173,25 @@ def make_workload(
     return wl
 
 
-# The five workloads of the benchmark plan, seeds 1000 + i.
-def config(i: int, **overrides) -> Workload:
-    """Workload ``i`` (1-based) of the five standard shapes; ``overrides`` adjust it."""
-    if i == 1:
-        kw = dict(name="cfg1_T256_H1_dense", lengths=[256], H=1, seed=1001, state_mode="dense")
-    elif i == 2:
-        kw = dict(name="cfg2_1x4096_H12_paged", lengths=[4096], H=12, seed=1002,
-                  state_mode="paged", num_slots=64)
-    elif i == 3:
-        kw = dict(name="cfg3_1x16384_H12_paged_pad", lengths=[16384], H=12, seed=1003,
-                  state_mode="paged", num_slots=64, stride_pad=4096)
-    elif i == 4:
-        kw = dict(name="cfg4_varlen128_H12_paged", lengths=None, H=12, seed=1004,
-                  state_mode="paged", num_slots=256, has_initial="bernoulli",
-                  lengths_from_seed=(128, 0, 2048, 4))
-    elif i == 5:
-        kw = dict(name="cfg5_256xT1_H12_paged_bf16", lengths=[1] * 256, H=12, seed=1005,
-                  state_mode="paged", state_dtype="bf16", num_slots=512)
-    else:
-        raise ValueError(i)
+# The standard shapes: the small dense case the oracle finishes in seconds, the one-GPU
+# serving shapes (one long prompt of 4K or 16K tokens, a ragged varlen batch, a batch of
+# one-token sequences), each with a fixed seed.
+STANDARD = {
+    "dense_1x256_H1": dict(lengths=[256], H=1, seed=1001, state_mode="dense"),
+    "paged_1x4096_H12": dict(lengths=[4096], H=12, seed=1002, state_mode="paged", num_slots=64),
+    "paged_1x16384_H12_pad": dict(lengths=[16384], H=12, seed=1003, state_mode="paged", num_slots=64,
+                                  stride_pad=4096),
+    "paged_varlen128_H12": dict(lengths=None, H=12, seed=1004, state_mode="paged", num_slots=256,
+                                has_initial="bernoulli", lengths_from_seed=(128, 0, 2048, 4)),
+    "paged_256x1_H12_bf16": dict(lengths=[1] * 256, H=12, seed=1005, state_mode="paged",
+                                 state_dtype="bf16", num_slots=512),
+}
+
+
+def standard(name: str, **overrides) -> Workload:
+    """One of the standard shapes by name; ``overrides`` adjust it."""
+    if name not in STANDARD:
+        raise ValueError(f"unknown workload {name!r}; known: {sorted(STANDARD)}")
+    kw = dict(STANDARD[name], name=name)
     kw.update(overrides)
     return make_workload(**kw)

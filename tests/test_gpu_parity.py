@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 import torch
 
-from gated_delta_rule_pack_amd.workloads import config, make_workload
+from gated_delta_rule_pack_amd.workloads import standard, make_workload
 from tests.kda_harness import compare, run_gpu, untouched_slots_bitwise
 
 pytestmark = pytest.mark.gpu
@@ -19,8 +19,8 @@ def _say(msg):
     print(msg, flush=True)
 
 
-def test_cfg1_dense_T256_H1():
-    wl = config(1)
+def test_dense_1x256_H1():
+    wl = standard("dense_1x256_H1")
     _say(f"case {wl.name}")
     run = run_gpu(wl)
     e_out, e_state = compare(wl, run)
@@ -75,8 +75,8 @@ def test_gate_regimes_ref_blocks(lb, shift):
     _say(f"  lb {lb} shift {shift}: out {e_out:.3e} state {e_state:.3e}")
 
 
-def test_cfg2_1x4096_H12_paged_full():
-    wl = config(2)
+def test_paged_1x4096_H12_full():
+    wl = standard("paged_1x4096_H12")
     _say(f"case {wl.name}")
     run = run_gpu(wl)
     e_out, e_state = compare(wl, run)
@@ -84,8 +84,8 @@ def test_cfg2_1x4096_H12_paged_full():
     _say(f"  out {e_out:.3e} state {e_state:.3e}")
 
 
-def test_cfg3_1x16384_H12_padded_stride_sampled_heads():
-    wl = config(3)
+def test_paged_1x16384_H12_padded_stride_sampled_heads():
+    wl = standard("paged_1x16384_H12_pad")
     _say(f"case {wl.name}")
     run = run_gpu(wl)
     assert np.all(np.isfinite(run.out))
@@ -95,9 +95,9 @@ def test_cfg3_1x16384_H12_padded_stride_sampled_heads():
 
 
 @pytest.mark.parametrize("lb,shift", [(-5.0, 6.0), (-20.0, 6.0)])
-def test_cfg3_saturated_gates_nan_free(lb, shift):
+def test_1x16384_saturated_gates_nan_free(lb, shift):
     """~160 nats (lb -5, raw +6) and ~640 nats (lb -20) of decay per chunk stay NaN-free."""
-    wl = config(3, gate_shift=shift, lower_bound=lb)
+    wl = standard("paged_1x16384_H12_pad", gate_shift=shift, lower_bound=lb)
     _say(f"case {wl.name} lb={lb} shift={shift}")
     run = run_gpu(wl)
     assert np.all(np.isfinite(run.out))
@@ -105,8 +105,8 @@ def test_cfg3_saturated_gates_nan_free(lb, shift):
     _say(f"  head 3: out {e_out:.3e} state {e_state:.3e}")
 
 
-def test_cfg4_varlen128_sampled_sequences():
-    wl = config(4)
+def test_varlen128_sampled_sequences():
+    wl = standard("paged_varlen128_H12")
     lens = wl.info["lengths"]
     flags = wl.has_initial_state.tolist()
     empties = [i for i, x in enumerate(lens) if x == 0][:2]
@@ -122,8 +122,8 @@ def test_cfg4_varlen128_sampled_sequences():
 
 
 @pytest.mark.parametrize("state_dtype", ["bf16", "f16"])
-def test_cfg5_decode_like_state_bound(state_dtype):
-    wl = config(5, state_dtype=state_dtype)
+def test_256x1_decode_like_state_bound(state_dtype):
+    wl = standard("paged_256x1_H12_bf16", state_dtype=state_dtype)
     _say(f"case {wl.name} {state_dtype}")
     run = run_gpu(wl)
     e_out, e_state = compare(wl, run)
