@@ -3,7 +3,7 @@
 // Each (chunk, head) item fuses the pre-processing the pages describe as a separate pack
 // pass (aiter PR 4741, Optimizations Applied: q/k L2 norm, lower-bounded sigmoid gate,
 // beta sigmoid, zero padding as an exact no-op) with the chunk-parallel prep (same page,
-// Summary: "prep, parallel over chunks"):
+// Summary: the first of its two kernels, one program per chunk):
 //
 //   G      inclusive in-chunk cumsum of g = lb * sigmoid(g_raw), per key channel;
 //          padding rows have g = 0 so they carry the last valid row's G

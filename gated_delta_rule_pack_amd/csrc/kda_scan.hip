@@ -1,7 +1,8 @@
 // Serial scan kernel for chunkwise KDA prefill on gfx950.
 //
-// The state walk over each sequence's chunks (aiter PR 4741, Summary: "scan, the serial
-// state walk"), with paged or dense state read and written in-kernel (aiter PR 5754,
+// The serial pass over each sequence's chunks that carries the state (aiter PR 4741,
+// Summary: the second of its two kernels), with paged or dense state read and written
+// in-kernel (aiter PR 5754,
 // Technical Details) and fp16/bf16 state storage up-cast to fp32 on load and rounded to
 // nearest even on store (aiter PR 5249, What). Per chunk, with S the V x K state at the
 // chunk start and the prep tiles W, U, Q, K, P, E of the chunk:
