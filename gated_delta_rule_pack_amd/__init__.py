@@ -162,7 +162,8 @@ def workspace_bytes(args: _lib.FwdArgs) -> int:
 
 def chunk_fwd(q, k, v, g_raw, beta_raw, cu_seqlens, *, cu_seqlens_cpu=None, scale=None,
               lower_bound=-5.0, initial_state=None, output_final_state=False, state_cache=None,
-              state_indices=None, has_initial_state=None, out=None, workspace=None, stream=None):
+              state_indices=None, has_initial_state=None, out=None, workspace=None, stream=None,
+              context=None):
     """Chunkwise KDA prefill forward on the current (or given) stream.
 
     q, k, v: bf16 ``[1, T, H, 128]``; g_raw: ``[1, T, H, 128]`` fp32/bf16; beta_raw:
@@ -174,7 +175,8 @@ def chunk_fwd(q, k, v, g_raw, beta_raw, cu_seqlens, *, cu_seqlens_cpu=None, scal
     allowed) with ``state_indices`` int32 ``[N]`` and ``has_initial_state`` bool ``[N]``.
 
     Returns ``(out, final_state)``; ``final_state`` is None in paged mode (the pool is
-    updated in place) and when not requested.
+    updated in place) and when not requested. ``context`` defaults to the device's
+    shared :class:`Context`.
     """
     import torch
     device = q.device
@@ -203,7 +205,7 @@ def chunk_fwd(q, k, v, g_raw, beta_raw, cu_seqlens, *, cu_seqlens_cpu=None, scal
     need = int(lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(a)))
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
-    ctx = get_context(device)
+    ctx = context if context is not None else get_context(device)
     if stream is None:
         stream = torch.cuda.current_stream(device)
     rc = lib.kda_chunk_fwd(ctx.ptr, ctypes.byref(a), ctypes.c_void_p(workspace.data_ptr()),

@@ -55,6 +55,7 @@ class Stats(Structure):
         ("calls", c_uint64), ("cache_hits", c_uint64), ("cache_misses", c_uint64),
         ("blocking_syncs", c_uint64), ("d2h_reads", c_uint64), ("h2d_uploads", c_uint64),
         ("last_dv_split", c_int32), ("last_ref_block", c_int32), ("last_n_chunks", c_int64),
+        ("last_seg_len", c_int32), ("last_n_segments", c_int32),
     ]
 
     def as_dict(self):
@@ -121,6 +122,8 @@ def load() -> ctypes.CDLL:
     lib.kda_prepare_chunk_indices.argtypes = [P, c_int32, c_int32, P, c_int64, POINTER(c_int64)]
     lib.kda_dv_split.restype = c_int32
     lib.kda_dv_split.argtypes = [c_int32, c_int32, c_int32]
+    lib.kda_seg_len.restype = c_int32
+    lib.kda_seg_len.argtypes = [c_int32, c_int32, c_int64]
     lib.kda_ref_block.restype = c_int32
     lib.kda_ref_block.argtypes = [c_float]
     lib.kda_get_stats.restype = c_int
@@ -147,6 +150,6 @@ def status_str(code: int) -> str:
 EXPORTS = [
     "kda_ctx_create", "kda_ctx_create_with_runtime", "kda_ctx_destroy",
     "kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd_validate", "kda_chunk_fwd",
-    "kda_prepare_chunk_indices", "kda_dv_split", "kda_ref_block", "kda_fwd_args_size",
+    "kda_prepare_chunk_indices", "kda_dv_split", "kda_seg_len", "kda_ref_block", "kda_fwd_args_size",
     "kda_status_str", "kda_get_stats", "kda_reset_stats", "kda_profile_enable", "kda_profile_read",
 ]

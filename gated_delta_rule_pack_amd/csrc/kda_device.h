@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "kda_internal.h"
+
 namespace kda {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -40,9 +42,115 @@ __device__ __forceinline__ bf16x8 pack8(f32x4 a, f32x4 b) {
   return r;
 }
 
+// Eight fp32 values (a then b) as bf16 hi + lo operands.
+__device__ __forceinline__ void split8(f32x4 a, f32x4 b, bf16x8& hi, bf16x8& lo) {
+  hi = pack8(a, b);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    lo[i] = to_bf16(a[i] - from_bf16(hi[i]));
+    lo[4 + i] = to_bf16(b[i] - from_bf16(hi[4 + i]));
+  }
+}
+
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
 // Logistic function with the fast exponential; -inf -> 0, +inf -> 1.
 __device__ __forceinline__ float sigmoidf_fast(float x) { return 1.0f / (1.0f + __expf(-x)); }
+
+// ------------------------------------------------------------------ scan-side helpers
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Raw buffer resource word 3 for gfx9-family untyped loads.
+constexpr int kBufWord3 = 0x00020000;
+
+__device__ __forceinline__ bf16x8 bload8(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
+template <int SDT>
+__device__ __forceinline__ f32x4 load_state4(const void* plane, size_t off) {
+  if constexpr (SDT == kF32) {
+    return *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(plane) + off);
+  } else if constexpr (SDT == kF16) {
+    const _Float16* s = reinterpret_cast<const _Float16*>(plane) + off;
+    typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+    h4 v = *reinterpret_cast<const h4*>(s);
+    return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+  } else {
+    const __bf16* s = reinterpret_cast<const __bf16*>(plane) + off;
+    bf16x4 v = *reinterpret_cast<const bf16x4*>(s);
+    return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+  }
+}
+
+template <int SDT>
+__device__ __forceinline__ void store_state4(void* plane, size_t off, f32x4 x) {
+  if constexpr (SDT == kF32) {
+    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(plane) + off) = x;
+  } else if constexpr (SDT == kF16) {
+    typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+    h4 v = {(_Float16)x[0], (_Float16)x[1], (_Float16)x[2], (_Float16)x[3]};
+    *reinterpret_cast<h4*>(reinterpret_cast<_Float16*>(plane) + off) = v;
+  } else {
+    bf16x4 v = {to_bf16(x[0]), to_bf16(x[1]), to_bf16(x[2]), to_bf16(x[3])};
+    *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(plane) + off) = v;
+  }
+}
+
+template <int SDT>
+__device__ __forceinline__ size_t elem_size() {
+  return SDT == kF32 ? 4 : 2;
+}
+
+// The (sequence n, head h) state plane to read at the start (null: start from zero) and
+// the one to write at the end (null: not written).
+template <int SDT>
+__device__ __forceinline__ const void* state_in_plane(const Plan& p, int n, int h) {
+  if (p.in_mode == kStateDense)
+    return reinterpret_cast<const char*>(p.state_in) + ((size_t)n * p.stride0 + (size_t)h * kHead * kHead) * elem_size<SDT>();
+  if (p.in_mode == kStatePaged && p.flags[n])
+    return reinterpret_cast<const char*>(p.state_in) +
+           ((size_t)p.indices[n] * p.stride0 + (size_t)h * kHead * kHead) * elem_size<SDT>();
+  return nullptr;
+}
+
+template <int SDT>
+__device__ __forceinline__ void* state_out_plane(const Plan& p, int n, int h) {
+  if (p.out_mode == kStateDense)
+    return reinterpret_cast<char*>(p.state_out) + ((size_t)n * p.stride0 + (size_t)h * kHead * kHead) * elem_size<SDT>();
+  if (p.out_mode == kStatePaged)
+    return reinterpret_cast<char*>(p.state_out) +
+           ((size_t)p.indices[n] * p.stride0 + (size_t)h * kHead * kHead) * elem_size<SDT>();
+  return nullptr;
+}
+
+// Barrier for waves that touch LDS only with ds instructions: their LDS writes are
+// complete (lgkmcnt) before it and no LDS read moves above it.
+__device__ __forceinline__ void barrier_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding: vmcnt bits
+// [3:0] and [15:14], expcnt [6:4] = 7, lgkmcnt [11:8] = 15).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Wait until at most k chunks of L loads each are still in flight (k <= KMAX).
+template <int L, int KMAX>
+__device__ __forceinline__ void wait_chunks(int k) {
+  if constexpr (KMAX == 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (k >= KMAX) wait_vmcnt<KMAX * L>();
+    else wait_chunks<L, KMAX - 1>(k);
+  }
+}
 
 }  // namespace kda

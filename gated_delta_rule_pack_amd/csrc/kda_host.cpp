@@ -1,6 +1,7 @@
 // Host side of the KDA prefill library: argument validation, chunk metadata, the
 // content-keyed metadata cache with asynchronous uploads from pinned memory, and the
-// launch sequence (prep, then scan) on the caller's stream.
+// launch sequence (prep; for few long sequences the segment maps and their combination;
+// then the scan) on the caller's stream.
 //
 // Metadata handling follows aiter PR 6912 (Changes): tables are built from host bounds
 // when the caller has them (no read-back), otherwise the bounds are read back once;
@@ -62,7 +63,12 @@ int rt_dev_alloc(void*, void** p, size_t n) { return (int)hipMalloc(p, n); }
 int rt_dev_free(void*, void* p) { return (int)hipFree(p); }
 int rt_launch(void*, int kernel, const void* plan, void* s) {
   const kda::Plan& p = *reinterpret_cast<const kda::Plan*>(plan);
-  return kernel == 0 ? kda::launch_prep(p, s) : kda::launch_scan(p, s);
+  switch (kernel) {
+    case 0: return kda::launch_prep(p, s);
+    case 1: return kda::launch_scan(p, s);
+    case 2: return kda::launch_segmap(p, s);
+    default: return kda::launch_segcombine(p, s);
+  }
 }
 int rt_ev_create_timed(void*, void** ev) { return (int)hipEventCreate(reinterpret_cast<hipEvent_t*>(ev)); }
 int rt_ev_elapsed(void*, float* ms, void* a, void* b) {
@@ -80,20 +86,10 @@ inline size_t align4(size_t n) { return (n + 3) & ~size_t(3); }  // int32 count 
 struct Meta {
   int N = 0;
   int64_t n_chunks = 0;
-  size_t off_cu = 0, off_co = 0, off_table = 0, words = 0;  // in int32 units
+  int seg_len = 0;  // chunks per segment of the segmented scan, 0 = one segment per sequence
+  int n_seg = 0, n_maps = 0, n_multi = 0;
+  size_t off_cu = 0, off_co = 0, off_table = 0, off_seg = 0, off_m2s = 0, off_comb = 0, words = 0;  // int32 units
 };
-
-// Layout of the single int32 metadata buffer for N sequences and n_chunks chunks.
-Meta meta_layout(int N, int64_t n_chunks) {
-  Meta m;
-  m.N = N;
-  m.n_chunks = n_chunks;
-  m.off_cu = 0;
-  m.off_co = align4(N + 1);
-  m.off_table = m.off_co + align4(N + 1);
-  m.words = m.off_table + align4((size_t)2 * n_chunks);
-  return m;
-}
 
 int64_t count_chunks(const int32_t* cu, int N) {
   int64_t n = 0;
@@ -101,11 +97,51 @@ int64_t count_chunks(const int32_t* cu, int N) {
   return n;
 }
 
+int64_t max_seq_chunks(const int32_t* cu, int N) {
+  int64_t m = 0;
+  for (int i = 0; i < N; ++i) m = std::max<int64_t>(m, (cu[i + 1] - cu[i] + kChunk - 1) / kChunk);
+  return m;
+}
+
+// Segments of one sequence of nc chunks (an empty sequence has one empty segment).
+inline int segments_of(int64_t nc, int seg_len) {
+  if (seg_len <= 0 || nc <= seg_len) return 1;
+  return (int)((nc + seg_len - 1) / seg_len);
+}
+
+// Layout of the single int32 metadata buffer: token bounds [N+1], chunk offsets [N+1],
+// chunk table [n_chunks][2], segment table [n_seg][kSegInts], map-slot -> segment
+// [n_maps], multi-segment sequences [n_multi][4].
+Meta meta_layout(const int32_t* cu, int N, int seg_len) {
+  Meta m;
+  m.N = N;
+  m.n_chunks = count_chunks(cu, N);
+  m.seg_len = seg_len;
+  for (int i = 0; i < N; ++i) {
+    const int g = segments_of((cu[i + 1] - cu[i] + kChunk - 1) / kChunk, seg_len);
+    m.n_seg += g;
+    m.n_maps += g - 1;
+    m.n_multi += g > 1;
+  }
+  m.off_cu = 0;
+  m.off_co = align4(N + 1);
+  m.off_table = m.off_co + align4(N + 1);
+  m.off_seg = m.off_table + align4((size_t)2 * m.n_chunks);
+  m.off_m2s = m.off_seg + align4((size_t)kda::kSegInts * m.n_seg);
+  m.off_comb = m.off_m2s + align4(m.n_maps);
+  m.words = m.off_comb + align4((size_t)4 * m.n_multi);
+  return m;
+}
+
 void build_meta(const int32_t* cu, const Meta& m, int32_t* buf) {
   std::memset(buf, 0, m.words * sizeof(int32_t));
   int32_t* co = buf + m.off_co;
   int32_t* table = buf + m.off_table;
+  int32_t* seg = buf + m.off_seg;
+  int32_t* m2s = buf + m.off_m2s;
+  int32_t* comb = buf + m.off_comb;
   int64_t c = 0;
+  int s = 0, mbase = 0, k = 0;
   for (int i = 0; i <= m.N; ++i) buf[m.off_cu + i] = cu[i];
   for (int i = 0; i < m.N; ++i) {
     co[i] = (int32_t)c;
@@ -114,6 +150,23 @@ void build_meta(const int32_t* cu, const Meta& m, int32_t* buf) {
       table[2 * c] = i;
       table[2 * c + 1] = j;
     }
+    const int G = segments_of(nc, m.seg_len);
+    for (int g = 0; g < G; ++g, ++s) {
+      int32_t* e = seg + (size_t)kda::kSegInts * s;
+      e[0] = i;                                              // sequence
+      e[1] = g * m.seg_len;                                  // first chunk (within the sequence)
+      e[2] = G == 1 ? nc : std::min(m.seg_len, nc - g * m.seg_len);  // chunks
+      e[3] = g == 0 ? -1 : mbase + g - 1;                    // map slot holding the start state
+      e[4] = g == G - 1 ? -1 : mbase + g;                    // map slot this segment produces
+      if (g < G - 1) m2s[mbase + g] = s;
+    }
+    if (G > 1) {
+      comb[4 * k] = i;
+      comb[4 * k + 1] = mbase;
+      comb[4 * k + 2] = G - 1;
+      ++k;
+    }
+    mbase += G - 1;
   }
   co[m.N] = (int32_t)c;
 }
@@ -134,11 +187,19 @@ bool bounds_ok(const int32_t* cu, int N, int T) {
   return true;
 }
 
-int32_t dv_split_for(int32_t N, int32_t H, int32_t cus) {
-  const int64_t units = (int64_t)N * H;
+int32_t dv_split_for(int32_t units_n, int32_t H, int32_t cus) {
+  const int64_t units = (int64_t)units_n * H;
   for (int s : {8, 4, 2})
     if (units * s <= 2 * (int64_t)cus) return s;
   return 2;
+}
+
+// Segment length of the segmented scan: only few, long sequences are split (many
+// (sequence, head) units already fill the chip, and below 32 chunks the serial walk is
+// short); about 16 segments for the longest sequence, at least kSegMin chunks each.
+int32_t seg_len_for(int32_t N, int32_t H, int64_t max_chunks) {
+  if ((int64_t)N * H > 96 || max_chunks < 256) return 0;
+  return (int32_t)std::max<int64_t>(kda::kSegMin, (max_chunks + 7) / 8);
 }
 
 int32_t ref_block_for(float lb) {
@@ -159,7 +220,8 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 // ------------------------------------------------------------------ context
 struct CacheEntry {
-  std::vector<int32_t> bounds;  // key: the full bounds array
+  std::vector<int32_t> bounds;  // key: the full bounds array and the segment length
+  int seg_len = 0;
   uint64_t hash = 0;
   void* dev = nullptr;          // device metadata buffer
   size_t bytes = 0;
@@ -190,6 +252,7 @@ struct ProfileMarks {
 struct kda_ctx {
   kda_runtime rt{};
   int dv_split_override = 0;  // tuning only (KDA_DV_SPLIT), 0 = policy
+  int seg_len_override = -1;  // tuning only (KDA_SEG_LEN), -1 = policy, 0 = never segment
   bool profiling = false;
   std::vector<ProfileMarks> marks;       // recorded, not yet read
   std::vector<ProfileMarks> marks_free;  // reusable
@@ -264,12 +327,12 @@ kda_status record_use(kda_ctx* ctx, CacheEntry* e, void* stream) {
 }
 
 // Find or upload the metadata for these bounds.
-kda_status get_meta(kda_ctx* ctx, const int32_t* cu, int N, void* stream, CacheEntry** out) {
+kda_status get_meta(kda_ctx* ctx, const int32_t* cu, int N, int seg_len, void* stream, CacheEntry** out) {
   int capturing = 0;
   if (ctx->rt.stream_is_capturing(ctx->rt.user, stream, &capturing)) return hip_fail();
   const uint64_t hsh = hash_bounds(cu, N);
   for (CacheEntry* e : ctx->cache) {
-    if (e->hash == hsh && (int)e->bounds.size() == N + 1 &&
+    if (e->hash == hsh && e->seg_len == seg_len && (int)e->bounds.size() == N + 1 &&
         std::memcmp(e->bounds.data(), cu, (N + 1) * sizeof(int32_t)) == 0) {
       if (e->upload_stream != stream && e->upload_event) {
         if (ctx->rt.stream_wait_event(ctx->rt.user, stream, e->upload_event)) return hip_fail();
@@ -289,7 +352,7 @@ kda_status get_meta(kda_ctx* ctx, const int32_t* cu, int N, void* stream, CacheE
     evict_one(ctx);
     if (ctx->cache.size() == before) break;  // everything retained
   }
-  const Meta m = meta_layout(N, count_chunks(cu, N));
+  const Meta m = meta_layout(cu, N, seg_len);
   const size_t bytes = m.words * sizeof(int32_t);
 
   // Pinned staging slot: reuse only once its previous copy has completed.
@@ -312,6 +375,7 @@ kda_status get_meta(kda_ctx* ctx, const int32_t* cu, int N, void* stream, CacheE
   CacheEntry* e = new (std::nothrow) CacheEntry();
   if (!e) return KDA_ERR_HIP;
   e->bounds.assign(cu, cu + N + 1);
+  e->seg_len = seg_len;
   e->hash = hsh;
   e->meta = m;
   e->bytes = bytes;
@@ -364,6 +428,8 @@ int32_t kda_dv_split(int32_t n_seqs, int32_t H, int32_t cu_count) { return dv_sp
 
 int32_t kda_ref_block(float lower_bound) { return ref_block_for(lower_bound); }
 
+int32_t kda_seg_len(int32_t n_seqs, int32_t H, int64_t max_chunks) { return seg_len_for(n_seqs, H, max_chunks); }
+
 kda_status kda_chunk_fwd_validate(const kda_fwd_args* a) {
   if (!a) return KDA_ERR_INVALID_ARG;
   if (a->N < 1 || a->T < 0 || a->H < 1) return KDA_ERR_INVALID_ARG;
@@ -407,11 +473,34 @@ kda_status kda_chunk_fwd_validate(const kda_fwd_args* a) {
   return KDA_OK;
 }
 
+kda_status kda_chunk_fwd_validate(const kda_fwd_args* a);
+
+namespace {
+
+// Workspace: chunk records, then (when the call may be segmented) the segment maps and
+// the segment start states. Chunks over all sequences are at most ceil(T / 32) + N; a
+// segmented call has at most max_chunks / kSegMin maps.
+struct WsLayout {
+  size_t records = 0, maps = 0, starts = 0, total = 0;
+};
+
+WsLayout ws_layout(const kda_fwd_args* a) {
+  WsLayout w;
+  const int64_t max_chunks = ((int64_t)a->T + kChunk - 1) / kChunk + a->N;
+  w.records = (size_t)a->H * (size_t)max_chunks * kda::kRecBytes;
+  int64_t max_maps = 0;
+  if ((int64_t)a->N * a->H <= 96) max_maps = max_chunks / kda::kSegMin;
+  w.maps = w.records;
+  w.starts = w.maps + (size_t)max_maps * a->H * kda::kMapBytes;
+  w.total = w.starts + (size_t)max_maps * a->H * kda::kStartBytes;
+  return w;
+}
+
+}  // namespace
+
 size_t kda_chunk_fwd_workspace_bytes(const kda_fwd_args* a) {
   if (kda_chunk_fwd_validate(a) != KDA_OK) return 0;
-  // Chunks over all sequences are at most ceil(T / 32) + N (one partial chunk each).
-  const int64_t max_chunks = ((int64_t)a->T + kChunk - 1) / kChunk + a->N;
-  return (size_t)a->H * (size_t)max_chunks * kda::kRecBytes;
+  return ws_layout(a).total;
 }
 
 kda_status kda_prepare_chunk_indices(const int32_t* cu_host, int32_t n_seqs, int32_t chunk, int32_t* pairs_out,
@@ -446,6 +535,10 @@ kda_status kda_ctx_create_with_runtime(const kda_runtime* rt, int cu_count, kda_
   if (const char* e = std::getenv("KDA_DV_SPLIT")) {
     const int v = std::atoi(e);
     if (v == 2 || v == 4 || v == 8) ctx->dv_split_override = v;
+  }
+  if (const char* e = std::getenv("KDA_SEG_LEN")) {
+    const int v = std::atoi(e);
+    if (v == 0 || v >= kda::kSegMin) ctx->seg_len_override = v;
   }
   ctx->ring.resize(kRingSlots);
   *out = ctx;
@@ -535,9 +628,12 @@ kda_status kda_chunk_fwd(kda_ctx* ctx, const kda_fwd_args* a, void* ws, size_t w
     if (!bounds_ok(cu, a->N, a->T)) return KDA_ERR_INVALID_ARG;
   }
 
+  int seg_len = seg_len_for(a->N, a->H, max_seq_chunks(cu, a->N));
+  if (ctx->seg_len_override >= 0 && (int64_t)a->N * a->H <= 96) seg_len = ctx->seg_len_override;
   CacheEntry* e = nullptr;
-  st = get_meta(ctx, cu, a->N, stream, &e);
+  st = get_meta(ctx, cu, a->N, seg_len, stream, &e);
   if (st != KDA_OK) return st;
+  const WsLayout wl = ws_layout(a);
 
   kda::Plan p{};
   p.T = a->T;
@@ -547,7 +643,11 @@ kda_status kda_chunk_fwd(kda_ctx* ctx, const kda_fwd_args* a, void* ws, size_t w
   p.scale = a->scale;
   p.lower_bound = a->lower_bound;
   p.ref_block = ref_block_for(a->lower_bound);
-  p.dv_split = ctx->dv_split_override ? ctx->dv_split_override : dv_split_for(a->N, a->H, ctx->cu_count);
+  p.n_seg = e->meta.n_seg;
+  p.n_maps = e->meta.n_maps;
+  p.n_multi = e->meta.n_multi;
+  p.seg_len = e->meta.seg_len;
+  p.dv_split = ctx->dv_split_override ? ctx->dv_split_override : dv_split_for(p.n_seg, a->H, ctx->cu_count);
   p.q = a->q;
   p.k = a->k;
   p.v = a->v;
@@ -559,6 +659,9 @@ kda_status kda_chunk_fwd(kda_ctx* ctx, const kda_fwd_args* a, void* ws, size_t w
   p.d_cu = base + e->meta.off_cu;
   p.d_co = base + e->meta.off_co;
   p.d_table = base + e->meta.off_table;
+  p.d_seg = base + e->meta.off_seg;
+  p.d_m2s = base + e->meta.off_m2s;
+  p.d_comb = base + e->meta.off_comb;
   p.state_dtype = a->state_dtype == KDA_F32 ? kda::kF32 : (a->state_dtype == KDA_F16 ? kda::kF16 : kda::kBF16);
   const int64_t plane = (int64_t)a->H * kHead * kHead;
   if (a->state_cache) {
@@ -578,6 +681,8 @@ kda_status kda_chunk_fwd(kda_ctx* ctx, const kda_fwd_args* a, void* ws, size_t w
   p.flags = a->has_initial_state;
   p.out = a->out;
   p.ws = ws;
+  p.maps = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + wl.maps);
+  p.starts = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + wl.starts);
   p.cu_count = ctx->cu_count;
 
   ProfileMarks pm{};
@@ -594,6 +699,10 @@ kda_status kda_chunk_fwd(kda_ctx* ctx, const kda_fwd_args* a, void* ws, size_t w
   }
   if (rt.launch(rt.user, 0, &p, stream)) return hip_fail();
   if (ctx->profiling && rt.event_record(rt.user, pm.ev[1], stream)) return hip_fail();
+  if (p.n_maps > 0) {
+    if (rt.launch(rt.user, 2, &p, stream)) return hip_fail();
+    if (rt.launch(rt.user, 3, &p, stream)) return hip_fail();
+  }
   if (rt.launch(rt.user, 1, &p, stream)) return hip_fail();
   if (ctx->profiling && rt.event_record(rt.user, pm.ev[2], stream)) return hip_fail();
   st = record_use(ctx, e, stream);
@@ -602,6 +711,8 @@ kda_status kda_chunk_fwd(kda_ctx* ctx, const kda_fwd_args* a, void* ws, size_t w
   ctx->stats.last_dv_split = p.dv_split;
   ctx->stats.last_ref_block = p.ref_block;
   ctx->stats.last_n_chunks = e->meta.n_chunks;
+  ctx->stats.last_seg_len = e->meta.seg_len;
+  ctx->stats.last_n_segments = e->meta.n_seg;
   return KDA_OK;
 }
 

@@ -15,7 +15,7 @@ constexpr int kThreadsScan = 256;
 // Per (head, chunk) workspace record written by prep and read by scan. Every tile is
 // stored in the exact per-lane order the scan's MFMA operands use, so the scan issues
 // one contiguous 16-byte load per lane per fragment.
-//   W  : 8 fragments (row tile t in 0..1, key block m in 0..3), bf16
+//   W  : 8 fragments (row tile t in 0..1, key block m in 0..3), bf16, stored negated (-W)
 //   Q  : 8 fragments, same order, bf16 (scale folded in)
 //   K  : 8 fragments (key tile 0..7), bf16
 //   U  : 8 fragments (value slice 0..7 of 16 channels), bf16
@@ -30,6 +30,18 @@ constexpr size_t kRecP = kRecU + 8 * kFrag;
 constexpr size_t kRecE = kRecP + 2 * kFrag;
 constexpr size_t kRecBytes = kRecE + kHead * 4;  // 35328 = 138 * 256
 static_assert(kRecBytes % 256 == 0, "records stay 256-byte aligned");
+
+// Segmented scan. A sequence of nc chunks is split into segments of seg_len chunks (the
+// last one shorter). Each chunk acts on the state as the affine map S -> S M + B
+// (M = Diag(e^{G_C}) - W^T K, B = U^T K); each segment but a sequence's last gets its
+// composed map (A, C) from the segment-map kernel, the combine kernel walks the maps to
+// every segment's start state, and the scan then runs all segments in parallel.
+constexpr int kSegMin = 8;        // shortest segment (chunks)
+constexpr int kSegInts = 8;       // segment table record: sequence, first chunk, chunks,
+                                  // start-state map slot (-1: the call's initial state),
+                                  // own map slot (-1: last segment, writes the final state)
+constexpr size_t kMapBytes = (size_t)2 * kHead * kHead * 4;  // A and C, fp32, [k][v] each
+constexpr size_t kStartBytes = (size_t)kHead * kHead * 4;    // start state, fp32, [v][k]
 
 enum StateMode : int { kStateNone = 0, kStateDense = 1, kStatePaged = 2 };
 enum DType : int { kF32 = 0, kF16 = 1, kBF16 = 2 };
@@ -49,6 +61,10 @@ struct Plan {
   const int32_t* d_cu;     // [N+1] token bounds (device)
   const int32_t* d_co;     // [N+1] chunk offsets (device)
   const int32_t* d_table;  // [n_chunks][2] (sequence, chunk within sequence) (device)
+  int n_seg, n_maps, n_multi, seg_len;
+  const int32_t* d_seg;    // [n_seg][kSegInts] segment table (device)
+  const int32_t* d_m2s;    // [n_maps] segment of each map slot (device)
+  const int32_t* d_comb;   // [n_multi][4] (sequence, first map slot, maps, 0) (device)
   int state_dtype;
   const void* state_in;
   int in_mode;
@@ -59,11 +75,15 @@ struct Plan {
   const uint8_t* flags;
   void* out;
   void* ws;             // first chunk record (256-byte aligned)
+  float* maps;          // [n_maps][H][2][K][V] segment maps A, C (S^T layout, fp32)
+  float* starts;        // [n_maps][H][V][K] state at the start of the segment after map slot m
   int cu_count;         // compute units of the device (persistent grid sizing)
 };
 
 // Launchers (defined in the .hip files). Return 0 on success, nonzero HIP error code.
 int launch_prep(const Plan& p, void* stream);
 int launch_scan(const Plan& p, void* stream);
+int launch_segmap(const Plan& p, void* stream);
+int launch_segcombine(const Plan& p, void* stream);
 
 }  // namespace kda

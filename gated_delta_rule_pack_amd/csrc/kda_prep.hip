@@ -10,7 +10,8 @@
 //   A      A[r,i] = beta_r sum_c k_r k_i e^{G_r - G_i}          (i < r)
 //   P      P[r,i] = scale sum_c q_r k_i e^{G_r - G_i}           (i <= r)
 //   T      (I + A)^{-1}, unit lower triangular, fp32
-//   W, U   T diag(beta) (k * e^G),  T diag(beta) v
+//   W, U   T diag(beta) (k * e^G),  T diag(beta) v; the record holds -W, so that the
+//          scan's Delta = U - W S^T is an MFMA accumulation started from U
 //   Q, K   scale * q * e^G,  k * e^{G_C - G};  E = e^{G_C}
 //
 // A and P use a bounded factorisation of the decay (same page, Optimizations Applied:
@@ -492,7 +493,7 @@ __device__ void process_item(const Plan& p, const Item& it, const Inputs& in, ch
     }
 #pragma unroll
     for (int t = 0; t < 2; ++t)
-      *reinterpret_cast<bf16x8*>(rec + kRecW + (size_t)(t * 4 + w) * kFrag + lane * 16) = pack8(dw[t][0], dw[t][1]);
+      *reinterpret_cast<bf16x8*>(rec + kRecW + (size_t)(t * 4 + w) * kFrag + lane * 16) = pack8(-dw[t][0], -dw[t][1]);
 #pragma unroll
     for (int q2 = 0; q2 < 2; ++q2)
       *reinterpret_cast<bf16x8*>(rec + kRecU + (size_t)(2 * w + q2) * kFrag + lane * 16) = pack8(du[0][q2], du[1][q2]);

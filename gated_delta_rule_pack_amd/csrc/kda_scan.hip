@@ -6,12 +6,15 @@
 // fp32 on load and rounded to nearest even on store (aiter PR 5249, What). Per chunk,
 // with S the V x K state at the chunk start and the prep tiles W, U, Q, K, P, E:
 //
-//   Delta = U - W S^T                    (the chunk's delta rows)
+//   Delta = U - W S^T                    (the chunk's delta rows; the record holds -W,
+//                                         so this is an MFMA accumulation from U)
 //   O     = Q S^T + P Delta              (scale folded into Q and P in prep)
 //   S     = S Diag(E) + Delta^T K
 //
-// One workgroup per (sequence, head, value slice of 16*NT channels); the slice count is
-// the host's occupancy-aware dv_split. Every slice of a (sequence, head) needs the whole
+// One workgroup per (segment, head, value slice of 16*NT channels); a segment is a whole
+// sequence unless the call is segmented, then it starts from the state the combine
+// kernel computed and only a sequence's last segment writes the final state. The slice
+// count is the host's occupancy-aware dv_split. Every slice of a (sequence, head) needs the whole
 // W, K, Q and P of each chunk, so a step costs about the same number of bytes through
 // one CU's vector-memory path whatever the slice width; at one workgroup per CU that
 // path, and the dependent MFMA/LDS chain of the state update, bound a step.
@@ -30,7 +33,7 @@
 // Wide slices (64 channels; many units), 4 waves, two workgroups per CU:
 //   * waves 0 and 1 each hold the state for half of the keys and exchange partial
 //     W S^T through LDS (64 value channels do not fit one wave's registers);
-//   * waves 2 and 3 rebuild Delta from the partials and form the output;
+//   * waves 2 and 3 add up Delta from the partials and form the output;
 //   every wave loads its own fragments, a few chunks ahead.
 
 #include <hip/hip_runtime.h>
@@ -41,106 +44,14 @@
 namespace kda {
 namespace {
 
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
-// Raw buffer resource word 3 for gfx9-family untyped loads.
-constexpr int kBufWord3 = 0x00020000;
-
-__device__ __forceinline__ bf16x8 bload8(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
-  return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
-}
-
-template <int SDT>
-__device__ __forceinline__ f32x4 load_state4(const void* plane, size_t off) {
-  if constexpr (SDT == kF32) {
-    return *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(plane) + off);
-  } else if constexpr (SDT == kF16) {
-    const _Float16* s = reinterpret_cast<const _Float16*>(plane) + off;
-    typedef _Float16 h4 __attribute__((ext_vector_type(4)));
-    h4 v = *reinterpret_cast<const h4*>(s);
-    return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
-  } else {
-    const __bf16* s = reinterpret_cast<const __bf16*>(plane) + off;
-    bf16x4 v = *reinterpret_cast<const bf16x4*>(s);
-    return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
-  }
-}
-
-template <int SDT>
-__device__ __forceinline__ void store_state4(void* plane, size_t off, f32x4 x) {
-  if constexpr (SDT == kF32) {
-    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(plane) + off) = x;
-  } else if constexpr (SDT == kF16) {
-    typedef _Float16 h4 __attribute__((ext_vector_type(4)));
-    h4 v = {(_Float16)x[0], (_Float16)x[1], (_Float16)x[2], (_Float16)x[3]};
-    *reinterpret_cast<h4*>(reinterpret_cast<_Float16*>(plane) + off) = v;
-  } else {
-    bf16x4 v = {to_bf16(x[0]), to_bf16(x[1]), to_bf16(x[2]), to_bf16(x[3])};
-    *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(plane) + off) = v;
-  }
-}
-
-template <int SDT>
-__device__ __forceinline__ size_t elem_size() {
-  return SDT == kF32 ? 4 : 2;
-}
-
-// The (sequence n, head h) state plane to read at the start (null: start from zero) and
-// the one to write at the end (null: not written).
-template <int SDT>
-__device__ __forceinline__ const void* state_in_plane(const Plan& p, int n, int h) {
-  if (p.in_mode == kStateDense)
-    return reinterpret_cast<const char*>(p.state_in) + ((size_t)n * p.stride0 + (size_t)h * kHead * kHead) * elem_size<SDT>();
-  if (p.in_mode == kStatePaged && p.flags[n])
-    return reinterpret_cast<const char*>(p.state_in) +
-           ((size_t)p.indices[n] * p.stride0 + (size_t)h * kHead * kHead) * elem_size<SDT>();
-  return nullptr;
-}
-
-template <int SDT>
-__device__ __forceinline__ void* state_out_plane(const Plan& p, int n, int h) {
-  if (p.out_mode == kStateDense)
-    return reinterpret_cast<char*>(p.state_out) + ((size_t)n * p.stride0 + (size_t)h * kHead * kHead) * elem_size<SDT>();
-  if (p.out_mode == kStatePaged)
-    return reinterpret_cast<char*>(p.state_out) +
-           ((size_t)p.indices[n] * p.stride0 + (size_t)h * kHead * kHead) * elem_size<SDT>();
-  return nullptr;
-}
-
-// Barrier for waves that touch LDS only with ds instructions: their LDS writes are
-// complete (lgkmcnt) before it and no LDS read moves above it.
-__device__ __forceinline__ void barrier_lds() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
-// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding: vmcnt bits
-// [3:0] and [15:14], expcnt [6:4] = 7, lgkmcnt [11:8] = 15).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-
-// Wait until at most k chunks of L loads each are still in flight (k <= KMAX).
-template <int L, int KMAX>
-__device__ __forceinline__ void wait_chunks(int k) {
-  if constexpr (KMAX == 0) {
-    wait_vmcnt<0>();
-  } else {
-    if (k >= KMAX) wait_vmcnt<KMAX * L>();
-    else wait_chunks<L, KMAX - 1>(k);
-  }
-}
-
-// Which (sequence, head, value group) a workgroup serves. Workgroups are dealt
-// round-robin to the 8 XCDs; all value groups of one (sequence, head) land on one XCD,
-// so its records are fetched into that XCD's L2 once.
+// Which (segment, head, value group) a workgroup serves. Workgroups are dealt
+// round-robin to the 8 XCDs; all value groups of one (segment, head) land on one XCD,
+// so its records are fetched into that XCD's L2 once. A segment is a run of one
+// sequence's chunks (the whole sequence unless the call is segmented).
 struct Unit {
   int n, h, grp;
+  int c0, nch;         // first chunk within the sequence, chunks
+  int m_prev, m_self;  // start-state map slot (-1: initial state), own map slot (-1: last)
 };
 
 __device__ __forceinline__ bool unit_of(const Plan& p, int units, int groups, Unit& u) {
@@ -151,29 +62,35 @@ __device__ __forceinline__ bool unit_of(const Plan& p, int units, int groups, Un
   u.grp = slot8 - local * groups;
   const int id = local * 8 + xcd;
   if (id >= units) return false;
-  u.n = id / p.H;
-  u.h = id - u.n * p.H;
+  const int s = id / p.H;
+  u.h = id - s * p.H;
+  const int32_t* e = p.d_seg + (size_t)kSegInts * s;
+  u.n = e[0];
+  u.c0 = e[1];
+  u.nch = e[2];
+  u.m_prev = e[3];
+  u.m_self = e[4];
   return true;
 }
 
+// One state row group of four: the segment's start state (fp32, from the combine
+// kernel), the call's initial state, or zero.
+template <int SDT>
+__device__ __forceinline__ f32x4 load_start4(const Plan& p, const Unit& u, const void* in_plane, size_t off) {
+  if (u.m_prev >= 0) return load_state4<kF32>(p.starts + ((size_t)u.m_prev * p.H + u.h) * kHead * kHead, off);
+  return in_plane ? load_state4<SDT>(in_plane, off) : zero4();
+}
+
 // Output-tile fragments one output wave consumes per chunk (row tile t).
-template <int NT, bool WITH_U>
 struct OutFrags {
-  bf16x8 q[4];                // Q fragments (t, key block m)
-  bf16x8 p;                   // P fragment of row tile t
-  bf16x8 u[WITH_U ? NT : 1];  // U fragments (wide kernel: to rebuild Delta)
+  bf16x8 q[4];  // Q fragments (t, key block m)
+  bf16x8 p;     // P fragment of row tile t
 };
 
-template <int NT, bool WITH_U>
-__device__ __forceinline__ void load_out_frags(OutFrags<NT, WITH_U>& f, __amdgpu_buffer_rsrc_t rs, int coff, int vo,
-                                               int t, int vtile0) {
+__device__ __forceinline__ void load_out_frags(OutFrags& f, __amdgpu_buffer_rsrc_t rs, int coff, int vo, int t) {
 #pragma unroll
   for (int m = 0; m < 4; ++m) f.q[m] = bload8(rs, vo, coff + (int)kRecQ + (t * 4 + m) * (int)kFrag);
   f.p = bload8(rs, vo, coff + (int)kRecP + t * (int)kFrag);
-  if constexpr (WITH_U) {
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) f.u[nt] = bload8(rs, vo, coff + (int)kRecU + (vtile0 + nt) * (int)kFrag);
-  }
 }
 
 // Runs step(f[j], c) for every chunk c < nc with DEPTH chunks of fragments in flight:
@@ -232,9 +149,10 @@ __global__ __launch_bounds__(256, 1) void scan_narrow(Plan p, int units, int gro
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, g4 = lane >> 4, l16 = lane & 15;
   const int vtile0 = un.grp * NT;  // first 16-channel value tile of this workgroup
-  const int cu0 = p.d_cu[n], cu1 = p.d_cu[n + 1];
-  const int nc = (cu1 - cu0 + kChunk - 1) / kChunk;
-  const char* rec0 = reinterpret_cast<const char*>(p.ws) + ((size_t)h * p.n_chunks + p.d_co[n]) * kRecBytes;
+  const int cu0 = p.d_cu[n] + kChunk * un.c0, cu1 = p.d_cu[n + 1];  // segment start, sequence end
+  const int nc = un.nch;
+  const char* rec0 =
+      reinterpret_cast<const char*>(p.ws) + ((size_t)h * p.n_chunks + p.d_co[n] + un.c0) * kRecBytes;
   const __amdgpu_buffer_rsrc_t rs =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(rec0), (short)0, nc * (int)kRecBytes, kBufWord3);
   const int vo = lane * 16;  // lane offset inside a fragment
@@ -292,28 +210,45 @@ __global__ __launch_bounds__(256, 1) void scan_narrow(Plan p, int units, int gro
 #pragma unroll
       for (int tt = 0; tt < 8; ++tt) {
         const size_t off = (size_t)(16 * (vtile0 + nt) + l16) * kHead + 16 * tt + 4 * g4;
-        S[nt][tt] = in_plane ? load_state4<SDT>(in_plane, off) : zero4();
+        S[nt][tt] = load_start4<SDT>(p, un, in_plane, off);
       }
 
     // One chunk's fragments, read from its ring slot.
+    // Issued together, in order of first use and pinned in that order (the scheduler
+    // would otherwise sink each read to its use or permute them): the LDS counter can
+    // name at most 15 reads in flight, so the wait before the first MFMA then covers
+    // only W, U and little else.
     struct Frags {
-      bf16x8 w[2][4];  // W (row tile t, key block m)
+      bf16x8 w[2][4];  // -W (row tile t, key block m)
+      bf16x8 u[NT];    // U of this workgroup's value tiles
       bf16x8 k[8];     // K (key tile)
-      bf16x8 u[NT];    // U (value tiles of this workgroup)
       f32x4 e[8];      // exp(G_C) of this lane's keys 16*tt + 4*g4 + i
     };
     auto read = [&](Frags& f, int slot) {
       const char* sl = lds + slot * L::kSlot;
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int m = 0; m < 4; ++m) f.w[t][m] = *reinterpret_cast<const bf16x8*>(sl + L::kSlotW + (t * 4 + m) * 1024 + vo);
+        for (int m = 0; m < 4; ++m) {
+          f.w[t][m] = *reinterpret_cast<const bf16x8*>(sl + L::kSlotW + (t * 4 + m) * 1024 + vo);
+          __builtin_amdgcn_sched_barrier(0);
+        }
 #pragma unroll
-      for (int tt = 0; tt < 8; ++tt) f.k[tt] = *reinterpret_cast<const bf16x8*>(sl + L::kSlotK + tt * 1024 + vo);
+      for (int nt = 0; nt < NT; ++nt) {
+        f.u[nt] = *reinterpret_cast<const bf16x8*>(sl + L::kSlotU + nt * 1024 + vo);
+        __builtin_amdgcn_sched_barrier(0);
+      }
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) f.u[nt] = *reinterpret_cast<const bf16x8*>(sl + L::kSlotU + nt * 1024 + vo);
+      for (int tt = 0; tt < 8; ++tt) {
+        f.k[tt] = *reinterpret_cast<const bf16x8*>(sl + L::kSlotK + tt * 1024 + vo);
+        __builtin_amdgcn_sched_barrier(0);
+      }
 #pragma unroll
-      for (int tt = 0; tt < 8; ++tt) f.e[tt] = *reinterpret_cast<const f32x4*>(sl + L::kSlotE + (16 * tt + 4 * g4) * 4);
+      for (int tt = 0; tt < 8; ++tt) {
+        f.e[tt] = *reinterpret_cast<const f32x4*>(sl + L::kSlotE + (16 * tt + 4 * g4) * 4);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     };
 
     if (nc > 0) {
@@ -329,43 +264,49 @@ __global__ __launch_bounds__(256, 1) void scan_narrow(Plan p, int units, int gro
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-          for (int m = 0; m < 4; ++m) {
-            Sb[nt][m] = pack8(S[nt][2 * m], S[nt][2 * m + 1]);
-            *reinterpret_cast<bf16x8*>(lds + L::sb(par, nt, m) + vo) = Sb[nt][m];
+          for (int m = 0; m < 4; ++m) Sb[nt][m] = pack8(S[nt][2 * m], S[nt][2 * m + 1]);
+        // Delta = U + (-W) S^T, accumulated from U; rows {4g..4g+3, 16+4g..16+4g+3} of
+        // the chunk per lane.
+        f32x4 x[NT][2];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            f32x4 a;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a[i] = from_bf16(f.u[nt][4 * t + i]);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) a = mfma(f.w[t][m], Sb[nt][m], a);
+            x[nt][t] = a;
           }
-        // Delta = U - W S^T; rows {4g..4g+3, 16+4g..16+4g+3} of the chunk per lane.
+        // Publish the state copy after the MFMAs are issued (they need only registers).
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int m = 0; m < 4; ++m) *reinterpret_cast<bf16x8*>(lds + L::sb(par, nt, m) + vo) = Sb[nt][m];
+        // Diag(E) S^T while the MFMAs above run.
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int tt = 0; tt < 8; ++tt) S[nt][tt] = S[nt][tt] * f.e[tt];
         bf16x8 Db[NT];
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-          f32x4 x[2];
-#pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            f32x4 a = mfma(f.w[t][0], Sb[nt][0], zero4());
-#pragma unroll
-            for (int m = 1; m < 4; ++m) a = mfma(f.w[t][m], Sb[nt][m], a);
-            x[t] = a;
-          }
-          f32x4 d0, d1;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            d0[i] = from_bf16(f.u[nt][i]) - x[0][i];
-            d1[i] = from_bf16(f.u[nt][4 + i]) - x[1][i];
-          }
-          Db[nt] = pack8(d0, d1);
+          Db[nt] = pack8(x[nt][0], x[nt][1]);
           *reinterpret_cast<bf16x8*>(lds + L::db(par, nt) + vo) = Db[nt];
         }
         // S^T = Diag(E) S^T + K^T Delta.
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-          for (int tt = 0; tt < 8; ++tt) S[nt][tt] = mfma(f.k[tt], Db[nt], S[nt][tt] * f.e[tt]);
+          for (int tt = 0; tt < 8; ++tt) S[nt][tt] = mfma(f.k[tt], Db[nt], S[nt][tt]);
         barrier_lds();  // publishes Sb, Db; the loader has chunk c + 1 in the next slot
         slot = (slot + 1 == RING) ? 0 : slot + 1;
         if (c + 1 < nc) read(f, slot);
       }
     }
 
-    void* out_plane = state_out_plane<SDT>(p, n, h);
+    void* out_plane = un.m_self < 0 ? state_out_plane<SDT>(p, n, h) : nullptr;
     if (out_plane) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
@@ -382,11 +323,11 @@ __global__ __launch_bounds__(256, 1) void scan_narrow(Plan p, int units, int gro
     // Lane holds O^T rows v = 16*(vtile0+nt) + 4*g4 .. +3 of token row 16*t + l16.
     const int orow = 16 * t + l16;
     const size_t ooff = (size_t)orow * row_stride + (size_t)h * kHead + 16 * vtile0 + 4 * g4;
-    typedef OutFrags<NT, false> F;
+    typedef OutFrags F;
     if (nc > 0) {
       barrier_lds();  // pairs with the first barrier of the other waves
       pipelined_chunks<DOUT, F>(
-          nc, [&](F& f, int c) { load_out_frags<NT, false>(f, rs, c * (int)kRecBytes, vo, t, vtile0); },
+          nc, [&](F& f, int c) { load_out_frags(f, rs, c * (int)kRecBytes, vo, t); },
           [&](const F& f, int c) {
             const int par = c & 1;
             barrier_lds();  // the state wave has published chunk c's Sb and Db
@@ -414,7 +355,7 @@ __global__ __launch_bounds__(256, 1) void scan_narrow(Plan p, int units, int gro
 // ====================================================================== wide slices
 // LDS per chunk parity, in rows of 64 lanes x 16 bytes:
 //   Sb [2 state waves][NT][2 key blocks]   state copy (bf16 operand registers)
-//   X  [2 state waves][2 row tiles][NT]    partial W S^T
+//   X  [2 state waves][2 row tiles][NT]    partial (-W) S^T, wave 0's started from U
 //   E  [2 state waves]                     exp(G_C), 64 floats each
 template <int NT>
 struct WideLds {
@@ -431,10 +372,10 @@ struct WideLds {
 // Fragments a state wave of the wide kernel consumes per chunk.
 template <int NT>
 struct WideStateFrags {
-  bf16x8 w[2][2];  // W fragments: row tile t, key block 2*wave + mm
+  bf16x8 w[2][2];  // -W fragments: row tile t, key block 2*wave + mm
   bf16x8 k[4];     // K fragments: key tiles 4*wave .. 4*wave + 3
-  bf16x8 u[NT];    // U fragments of this workgroup's value tiles
   float e;         // exp(G_C) of key 64*wave + lane
+  bf16x8 u[NT];    // U fragments of this workgroup's value tiles (wave 0 only)
 };
 
 template <int NT>
@@ -447,10 +388,13 @@ __device__ __forceinline__ void load_wide_state_frags(WideStateFrags<NT>& f, __a
       f.w[t][mm] = bload8(rs, vo, coff + (int)kRecW + (t * 4 + 2 * wave + mm) * (int)kFrag);
 #pragma unroll
   for (int tt = 0; tt < 4; ++tt) f.k[tt] = bload8(rs, vo, coff + (int)kRecK + (4 * wave + tt) * (int)kFrag);
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) f.u[nt] = bload8(rs, vo, coff + (int)kRecU + (vtile0 + nt) * (int)kFrag);
   // One float per lane (256 bytes per wave), redistributed through LDS.
   f.e = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, vo >> 2, coff + (int)kRecE + 256 * wave, 0));
+  // Last, so that the other loads' wait counts do not depend on whether U was loaded.
+  if (wave == 0) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) f.u[nt] = bload8(rs, vo, coff + (int)kRecU + (vtile0 + nt) * (int)kFrag);
+  }
 }
 
 template <int NT, int SDT, int DEPTH>
@@ -463,9 +407,10 @@ __global__ __launch_bounds__(256, 2) void scan_wide(Plan p, int units, int group
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, g4 = lane >> 4, l16 = lane & 15;
   const int vtile0 = un.grp * NT;
-  const int cu0 = p.d_cu[n], cu1 = p.d_cu[n + 1];
-  const int nc = (cu1 - cu0 + kChunk - 1) / kChunk;
-  const char* rec0 = reinterpret_cast<const char*>(p.ws) + ((size_t)h * p.n_chunks + p.d_co[n]) * kRecBytes;
+  const int cu0 = p.d_cu[n] + kChunk * un.c0, cu1 = p.d_cu[n + 1];  // segment start, sequence end
+  const int nc = un.nch;
+  const char* rec0 =
+      reinterpret_cast<const char*>(p.ws) + ((size_t)h * p.n_chunks + p.d_co[n] + un.c0) * kRecBytes;
   const __amdgpu_buffer_rsrc_t rs =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(rec0), (short)0, nc * (int)kRecBytes, kBufWord3);
   const int vo = lane * 16;
@@ -480,7 +425,7 @@ __global__ __launch_bounds__(256, 2) void scan_wide(Plan p, int units, int group
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) {
         const size_t off = (size_t)(16 * (vtile0 + nt) + l16) * kHead + 16 * (4 * wave + tt) + 4 * g4;
-        S[nt][tt] = in_plane ? load_state4<SDT>(in_plane, off) : zero4();
+        S[nt][tt] = load_start4<SDT>(p, un, in_plane, off);
       }
     typedef WideStateFrags<NT> F;
     if (nc > 0) {
@@ -496,13 +441,19 @@ __global__ __launch_bounds__(256, 2) void scan_wide(Plan p, int units, int group
                 Sb[nt][mm] = pack8(S[nt][2 * mm], S[nt][2 * mm + 1]);
                 wlds[L::sb(par, wave, nt, mm) + lane] = __builtin_bit_cast(u32x4, Sb[nt][mm]);
               }
-            // Partial W S^T over this wave's 64 keys, both row tiles.
+            // Partial (-W) S^T over this wave's 64 keys, both row tiles; wave 0 starts
+            // from U, so the two partials add up to Delta.
             f32x4 X[2][NT];
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
               for (int t = 0; t < 2; ++t) {
-                f32x4 a = mfma(f.w[t][0], Sb[nt][0], zero4());
+                f32x4 a = zero4();
+                if (wave == 0) {
+#pragma unroll
+                  for (int i = 0; i < 4; ++i) a[i] = from_bf16(f.u[nt][4 * t + i]);
+                }
+                a = mfma(f.w[t][0], Sb[nt][0], a);
                 a = mfma(f.w[t][1], Sb[nt][1], a);
                 X[t][nt] = a;
                 wlds[L::x(par, wave, t, nt) + lane] = __builtin_bit_cast(u32x4, a);
@@ -516,22 +467,16 @@ __global__ __launch_bounds__(256, 2) void scan_wide(Plan p, int units, int group
             for (int tt = 0; tt < 4; ++tt) E[tt] = *reinterpret_cast<const f32x4*>(eb + 16 * tt + 4 * g4);
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
-              // Full key sums; a + b == b + a, so every wave rebuilds identical bits.
-              const f32x4 x0 = X[0][nt] + __builtin_bit_cast(f32x4, wlds[L::x(par, wave ^ 1, 0, nt) + lane]);
-              const f32x4 x1 = X[1][nt] + __builtin_bit_cast(f32x4, wlds[L::x(par, wave ^ 1, 1, nt) + lane]);
-              f32x4 d0, d1;
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                d0[i] = from_bf16(f.u[nt][i]) - x0[i];
-                d1[i] = from_bf16(f.u[nt][4 + i]) - x1[i];
-              }
+              // Delta: a + b == b + a, so every wave rebuilds identical bits.
+              const f32x4 d0 = X[0][nt] + __builtin_bit_cast(f32x4, wlds[L::x(par, wave ^ 1, 0, nt) + lane]);
+              const f32x4 d1 = X[1][nt] + __builtin_bit_cast(f32x4, wlds[L::x(par, wave ^ 1, 1, nt) + lane]);
               const bf16x8 Db = pack8(d0, d1);
 #pragma unroll
               for (int tt = 0; tt < 4; ++tt) S[nt][tt] = mfma(f.k[tt], Db, S[nt][tt] * E[tt]);
             }
           });
     }
-    void* out_plane = state_out_plane<SDT>(p, n, h);
+    void* out_plane = un.m_self < 0 ? state_out_plane<SDT>(p, n, h) : nullptr;
     if (out_plane) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
@@ -547,10 +492,10 @@ __global__ __launch_bounds__(256, 2) void scan_wide(Plan p, int units, int group
     const size_t row_stride = (size_t)p.H * kHead;
     const int orow = 16 * t + l16;
     const size_t ooff = (size_t)orow * row_stride + (size_t)h * kHead + 16 * vtile0 + 4 * g4;
-    typedef OutFrags<NT, true> F;
+    typedef OutFrags F;
     if (nc > 0) {
       pipelined_chunks<DEPTH, F>(
-          nc, [&](F& f, int c) { load_out_frags<NT, true>(f, rs, c * (int)kRecBytes, vo, t, vtile0); },
+          nc, [&](F& f, int c) { load_out_frags(f, rs, c * (int)kRecBytes, vo, t); },
           [&](const F& f, int c) {
             const int par = c & 1;
             barrier_lds();  // the state waves have published chunk c's copies and partials
@@ -559,16 +504,10 @@ __global__ __launch_bounds__(256, 2) void scan_wide(Plan p, int units, int group
             __bf16* out_c = reinterpret_cast<__bf16*>(p.out) + (size_t)t0 * row_stride + ooff;
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
-              const f32x4 x0 = __builtin_bit_cast(f32x4, wlds[L::x(par, 0, 0, nt) + lane]) +
+              const f32x4 d0 = __builtin_bit_cast(f32x4, wlds[L::x(par, 0, 0, nt) + lane]) +
                                __builtin_bit_cast(f32x4, wlds[L::x(par, 1, 0, nt) + lane]);
-              const f32x4 x1 = __builtin_bit_cast(f32x4, wlds[L::x(par, 0, 1, nt) + lane]) +
+              const f32x4 d1 = __builtin_bit_cast(f32x4, wlds[L::x(par, 0, 1, nt) + lane]) +
                                __builtin_bit_cast(f32x4, wlds[L::x(par, 1, 1, nt) + lane]);
-              f32x4 d0, d1;
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                d0[i] = from_bf16(f.u[nt][i]) - x0[i];
-                d1[i] = from_bf16(f.u[nt][4 + i]) - x1[i];
-              }
               const bf16x8 Db = pack8(d0, d1);
               // (Q S^T)^T = S Q^T over all 128 keys: key block m lives in state wave m / 2.
               f32x4 o = zero4();
@@ -600,7 +539,7 @@ int set_lds_limit(KernelT* kernel, size_t bytes, bool& done) {
 template <int NT, int SDT>
 int launch_nt(const Plan& p, hipStream_t s) {
   const int groups = 8 / NT;
-  const int units = p.N * p.H;
+  const int units = p.n_seg * p.H;
   const int nblocks = 8 * ((units + 7) / 8) * groups;
   if constexpr (NT <= 2) {
     constexpr int R = 5;                 // ring slots: the loader runs 4 chunks ahead

@@ -113,6 +113,8 @@ typedef struct kda_stats {
   int32_t last_dv_split;   /* value-channel split used by the last scan launch */
   int32_t last_ref_block;  /* reference-row block used by the last prep launch */
   int64_t last_n_chunks;   /* chunks (over all sequences) in the last call */
+  int32_t last_seg_len;    /* segment length (chunks) of the last call's scan, 0 = unsegmented */
+  int32_t last_n_segments; /* segments (over all sequences) in the last call */
 } kda_stats;
 
 typedef struct kda_ctx kda_ctx;
@@ -140,7 +142,9 @@ typedef struct kda_runtime {
   int (*host_free_pinned)(void* user, void* ptr);
   int (*device_alloc)(void* user, void** ptr, size_t bytes);
   int (*device_free)(void* user, void* ptr);
-  /* kernel: 0 = prep, 1 = scan. plan is internal launch data, opaque to the runtime. */
+  /* kernel: 0 = prep, 1 = scan, 2 = segment maps, 3 = segment combine (2 and 3 only
+   * for a segmented call, between prep and scan). plan is internal launch data, opaque
+   * to the runtime. */
   int (*launch)(void* user, int kernel, const void* plan, void* stream);
   /* Timing events (used only while profiling is enabled). */
   int (*event_create_timed)(void* user, void** event);
@@ -156,14 +160,16 @@ kda_status kda_ctx_create_with_runtime(const kda_runtime* rt, int cu_count, kda_
 void kda_ctx_destroy(kda_ctx* ctx);
 
 /* Host-only, pure: bytes of caller workspace one call with these shapes needs
- * (depends on T, N, H only). 0 when the arguments are invalid. */
+ * (depends on T, N, H only: chunk records, plus room for segment maps and start states
+ * when N*H <= 96). 0 when the arguments are invalid. */
 size_t kda_chunk_fwd_workspace_bytes(const kda_fwd_args* args);
 
 /* Host-only: every argument check kda_chunk_fwd makes, touching no device memory. */
 kda_status kda_chunk_fwd_validate(const kda_fwd_args* args);
 
 /* Forward call. Validates, resolves metadata (cache hit, or one asynchronous upload from
- * pinned memory), then enqueues prep and scan on stream (a hipStream_t; null = default
+ * pinned memory), then enqueues prep, the segment kernels when the call is segmented,
+ * and scan on stream (a hipStream_t; null = default
  * stream) and returns without waiting. The workspace (caller-owned device memory of at
  * least kda_chunk_fwd_workspace_bytes(args) bytes, 256-byte aligned) must stay
  * allocated and unused by anything else until the stream work completes. */
@@ -178,10 +184,20 @@ kda_status kda_chunk_fwd(kda_ctx* ctx, const kda_fwd_args* args, void* workspace
 kda_status kda_prepare_chunk_indices(const int32_t* cu_host, int32_t n_seqs, int32_t chunk,
                                      int32_t* pairs_out, int64_t cap, int64_t* n_out);
 
-/* Value-channel split the scan uses for n_seqs sequences of H heads on cu_count compute
- * units (host-only, pure): the finest split in {8, 4, 2} with n_seqs*H*split <= 2*cu_count,
- * else 2 (aiter PR 4741, Optimizations Applied: occupancy-aware dv_split). */
+/* Value-channel split the scan uses for n_seqs scan units (sequences, or segments of a
+ * segmented call) of H heads on cu_count compute units (host-only, pure): the finest
+ * split in {8, 4, 2} with n_seqs*H*split <= 2*cu_count, else 2 (aiter PR 4741,
+ * Optimizations Applied: occupancy-aware dv_split). */
 int32_t kda_dv_split(int32_t n_seqs, int32_t H, int32_t cu_count);
+
+/* Segment length (chunks) of the segmented scan for n_seqs sequences of H heads whose
+ * longest sequence has max_chunks chunks (host-only, pure); 0 = not segmented. The pages
+ * split long sequences into segments (a pass that composes each segment, then a scan
+ * over segments; aiter PR 5754, Technical Details and Test Result; segment tables built
+ * from host bounds in the one metadata upload, aiter PR 6912, Changes). Here: only when
+ * n_seqs*H <= 96 and max_chunks >= 256; about 8 segments for the longest sequence, at
+ * least 8 chunks each. */
+int32_t kda_seg_len(int32_t n_seqs, int32_t H, int64_t max_chunks);
 
 /* Reference-row block the prep kernel uses for a gate lower bound (host-only, pure): the
  * largest s in {16, 8, 4, 2, 1} with (s - 1) * |lower_bound| <= 80, so that every factor

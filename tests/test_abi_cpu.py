@@ -142,14 +142,24 @@ def test_padded_stride_and_zero_tokens_accepted(lib):
     assert _check(lib, z) == _lib.KDA_OK
 
 
+MAP_BYTES = 2 * 128 * 128 * 4    # segment map A and C, fp32
+START_BYTES = 128 * 128 * 4      # segment start state, fp32
+
+
 def test_workspace_bytes(lib):
     bufs = FakeBufs()
-    for T, N, H in [(100, 3, 2), (4096, 1, 12), (0, 2, 1), (1, 1, 1)]:
+    for T, N, H in [(100, 3, 2), (4096, 1, 12), (0, 2, 1), (1, 1, 1), (5000, 9, 12), (16384, 8, 12)]:
         cu = np.linspace(0, T, N + 1).astype(np.int32)
         a, _, _ = _valid_args(bufs, T=T, N=N, H=H, cu=cu)
         if T == 0:
             a.q = a.k = a.v = a.g_raw = a.beta_raw = a.out = None
-        assert lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(a)) == H * ((T + 31) // 32 + N) * REC
+        max_chunks = (T + 31) // 32 + N
+        # Records; then, when the call may be segmented (N*H <= 96), room for the maps and
+        # start states of segments of at least 8 chunks.
+        want = H * max_chunks * REC
+        if N * H <= 96:
+            want += (max_chunks // 8) * H * (MAP_BYTES + START_BYTES)
+        assert lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(a)) == want
 
 
 # ---------------------------------------------------------------- chunk table, policies
@@ -187,6 +197,18 @@ def test_dv_split_and_ref_block_policies(lib):
     assert lib.kda_ref_block(-20.0) == 4
     assert lib.kda_ref_block(0.0) == 16
     assert lib.kda_ref_block(-200.0) == 1
+
+
+def test_segment_length_policy(lib):
+    # Few long sequences: about 8 segments for the longest, at least 8 chunks each.
+    assert lib.kda_seg_len(1, 12, 512) == 64
+    assert lib.kda_seg_len(1, 12, 500) == 63
+    assert lib.kda_seg_len(8, 12, 256) == 32
+    # Short sequences, or enough (sequence, head) units already: not segmented.
+    assert lib.kda_seg_len(1, 12, 128) == 0
+    assert lib.kda_seg_len(1, 12, 255) == 0
+    assert lib.kda_seg_len(9, 12, 1000) == 0
+    assert lib.kda_seg_len(128, 12, 64) == 0
 
 
 # ---------------------------------------------------------------- fake runtime
@@ -347,6 +369,61 @@ def test_host_bounds_issue_no_sync_and_one_upload(lib, fake):
     assert fake.syncs() == []
     st = _stats(lib, fake)
     assert st["cache_hits"] == 1 and st["calls"] == 2 and st["last_n_chunks"] == 11
+
+
+def _segments_reference(cu, L):
+    """Segments of each sequence: runs of L chunks (the last shorter), one empty segment
+    for an empty sequence; map slots numbered over all segments but each sequence's last."""
+    segs, m2s, comb, mbase = [], [], [], 0
+    for n in range(len(cu) - 1):
+        nc = -(-(int(cu[n + 1]) - int(cu[n])) // 32)
+        G = 1 if nc <= L else -(-nc // L)
+        for g in range(G):
+            c0 = g * L
+            nch = nc if G == 1 else min(L, nc - c0)
+            m_prev = -1 if g == 0 else mbase + g - 1
+            m_self = -1 if g == G - 1 else mbase + g
+            if m_self >= 0:
+                m2s.append(len(segs))
+            segs.append([n, c0, nch, m_prev, m_self, 0, 0, 0])
+        if G > 1:
+            comb.append([n, mbase, G - 1, 0])
+        mbase += G - 1
+    return np.array(segs, np.int32), np.array(m2s, np.int32), np.array(comb, np.int32).reshape(-1, 4)
+
+
+def test_segmented_call_launches_and_tables(lib, fake):
+    """A long sequence next to short and empty ones: segment maps and combine run between
+    prep and scan, and the uploaded segment tables match a plain reference."""
+    bufs = FakeBufs()
+    lens = [300 * 32 + 5, 0, 100, 40 * 32]   # 301, 0, 4 and 40 chunks
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    N, T, H = len(lens), int(cu[-1]), 2
+    a, _, _ = _valid_args(bufs, T=T, N=N, H=H, cu=cu, paged=True)
+    L = lib.kda_seg_len(N, H, 301)
+    assert L == 38
+    assert _call(lib, fake, a) == _lib.KDA_OK
+    assert fake.launches == [(0, 0x10), (2, 0x10), (3, 0x10), (1, 0x10)]
+    st = _stats(lib, fake)
+    segs, m2s, comb = _segments_reference(cu, L)
+    assert st["last_seg_len"] == L and st["last_n_segments"] == len(segs)
+    # Buffer layout: cu, chunk offsets, chunk table, segment table, map -> segment,
+    # multi-segment sequences; every block starts 16-byte aligned.
+    words = fake.uploads[0][3]
+    a4 = lambda n: (n + 3) // 4 * 4
+    n_chunks = int(sum(-(-x // 32) for x in lens))
+    off_seg = 2 * a4(N + 1) + a4(2 * n_chunks)
+    off_m2s = off_seg + a4(8 * len(segs))
+    off_comb = off_m2s + a4(len(m2s))
+    assert np.array_equal(words[off_seg:off_seg + 8 * len(segs)].reshape(-1, 8), segs)
+    assert np.array_equal(words[off_m2s:off_m2s + len(m2s)], m2s)
+    assert np.array_equal(words[off_comb:off_comb + 4 * len(comb)].reshape(-1, 4), comb)
+    # The segments tile every sequence's chunks exactly once, in order.
+    for n in range(N):
+        mine = segs[segs[:, 0] == n]
+        nc = -(-lens[n] // 32)
+        assert mine[0, 1] == 0 and mine[:, 2].sum() == nc
+        assert np.all(mine[1:, 1] == mine[:-1, 1] + mine[:-1, 2])
 
 
 def test_device_bounds_read_back_once(lib, fake):
