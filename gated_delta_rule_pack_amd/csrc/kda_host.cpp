@@ -187,11 +187,15 @@ bool bounds_ok(const int32_t* cu, int N, int T) {
   return true;
 }
 
+// Value-channel split of the scan: the finest split in {8, 4, 2} whose workgroups all
+// get a CU of their own, else the whole head per workgroup (1). Few units are bound by
+// the per-chunk latency (narrow slices shorten it); many by the chip's load bandwidth
+// (every split rereads the chunk's shared tiles, so coarse is cheaper).
 int32_t dv_split_for(int32_t units_n, int32_t H, int32_t cus) {
   const int64_t units = (int64_t)units_n * H;
   for (int s : {8, 4, 2})
-    if (units * s <= 2 * (int64_t)cus) return s;
-  return 2;
+    if (units * s <= (int64_t)cus) return s;
+  return 1;
 }
 
 // Segment length of the segmented scan: only few, long sequences are split (many
@@ -534,7 +538,7 @@ kda_status kda_ctx_create_with_runtime(const kda_runtime* rt, int cu_count, kda_
   // Tuning overrides, read once per context; the defaults are the documented policy.
   if (const char* e = std::getenv("KDA_DV_SPLIT")) {
     const int v = std::atoi(e);
-    if (v == 2 || v == 4 || v == 8) ctx->dv_split_override = v;
+    if (v == 1 || v == 2 || v == 4 || v == 8) ctx->dv_split_override = v;
   }
   if (const char* e = std::getenv("KDA_SEG_LEN")) {
     const int v = std::atoi(e);

@@ -40,7 +40,7 @@ constexpr int kSegMin = 8;        // shortest segment (chunks)
 constexpr int kSegInts = 8;       // segment table record: sequence, first chunk, chunks,
                                   // start-state map slot (-1: the call's initial state),
                                   // own map slot (-1: last segment, writes the final state)
-constexpr size_t kMapBytes = (size_t)2 * kHead * kHead * 4;  // A and C, fp32, [k][v] each
+constexpr size_t kMapBytes = (size_t)2 * kHead * kHead * 4;  // A (bf16 hi, lo), C (fp32), [k][v] each
 constexpr size_t kStartBytes = (size_t)kHead * kHead * 4;    // start state, fp32, [v][k]
 
 enum StateMode : int { kStateNone = 0, kStateDense = 1, kStatePaged = 2 };
@@ -75,7 +75,8 @@ struct Plan {
   const uint8_t* flags;
   void* out;
   void* ws;             // first chunk record (256-byte aligned)
-  float* maps;          // [n_maps][H][2][K][V] segment maps A, C (S^T layout, fp32)
+  float* maps;          // [n_maps][H] segment maps: A as bf16 hi and lo planes, then C fp32,
+                        // each [K][V] (S^T layout)
   float* starts;        // [n_maps][H][V][K] state at the start of the segment after map slot m
   int cu_count;         // compute units of the device (persistent grid sizing)
 };

@@ -185,9 +185,11 @@ kda_status kda_prepare_chunk_indices(const int32_t* cu_host, int32_t n_seqs, int
                                      int32_t* pairs_out, int64_t cap, int64_t* n_out);
 
 /* Value-channel split the scan uses for n_seqs scan units (sequences, or segments of a
- * segmented call) of H heads on cu_count compute units (host-only, pure): the finest
- * split in {8, 4, 2} with n_seqs*H*split <= 2*cu_count, else 2 (aiter PR 4741,
- * Optimizations Applied: occupancy-aware dv_split). */
+ * segmented call) of H heads on cu_count compute units (host-only, pure; aiter PR 4741,
+ * Optimizations Applied: occupancy-aware dv_split): the finest split in {8, 4, 2} with
+ * n_seqs*H*split <= cu_count, else 1. Every split of a head rereads the chunk's whole W,
+ * K, Q and P: fine splits shorten the serial chain of few units, the whole head per
+ * workgroup (1) spends the chip's load bandwidth best when there are many. */
 int32_t kda_dv_split(int32_t n_seqs, int32_t H, int32_t cu_count);
 
 /* Segment length (chunks) of the segmented scan for n_seqs sequences of H heads whose

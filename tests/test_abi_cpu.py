@@ -188,10 +188,12 @@ def test_chunk_table_matches_repeat_interleave_reference(lib, seed):
 
 def test_dv_split_and_ref_block_policies(lib):
     assert lib.kda_dv_split(1, 12, 256) == 8
-    assert lib.kda_dv_split(4, 12, 256) == 8
-    assert lib.kda_dv_split(8, 12, 256) == 4
-    assert lib.kda_dv_split(16, 12, 256) == 2
-    assert lib.kda_dv_split(128, 12, 256) == 2
+    assert lib.kda_dv_split(2, 12, 256) == 8
+    assert lib.kda_dv_split(3, 12, 256) == 4
+    assert lib.kda_dv_split(8, 12, 256) == 2
+    assert lib.kda_dv_split(10, 12, 256) == 2
+    assert lib.kda_dv_split(11, 12, 256) == 1
+    assert lib.kda_dv_split(128, 12, 256) == 1
     assert lib.kda_ref_block(-5.0) == 16
     assert lib.kda_ref_block(-5.4) == 8
     assert lib.kda_ref_block(-20.0) == 4
