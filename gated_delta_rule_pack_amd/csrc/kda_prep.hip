@@ -9,7 +9,8 @@
 //          padding rows have g = 0 so they carry the last valid row's G
 //   A      A[r,i] = beta_r sum_c k_r k_i e^{G_r - G_i}          (i < r)
 //   P      P[r,i] = scale sum_c q_r k_i e^{G_r - G_i}           (i <= r)
-//   T      (I + A)^{-1}, unit lower triangular, fp32
+//   T      (I + A)^{-1}, unit lower triangular, fp32: diagonal 16x16 blocks by forward
+//          substitution, the off-diagonal block -T11 A10 T00 on fp32 MFMA
 //   W, U   T diag(beta) (k * e^G),  T diag(beta) v; the record holds -W, so that the
 //          scan's Delta = U - W S^T is an MFMA accumulation started from U
 //   Q, K   scale * q * e^G,  k * e^{G_C - G};  E = e^{G_C}
@@ -55,16 +56,21 @@ constexpr int kTileTT = 32 * LDT * 2;           // 2560 B
 constexpr int kFactorBytes = 6 * kTileA;        // L_k hi/lo, L_q hi/lo, R hi/lo
 constexpr int kProductBytes = 4 * kTileT + kTileA + 2 * kTileTT;  // KG hi/lo, K^T, v^T, Q, T' hi/lo
 
+// REF = 16 (two row blocks) builds both blocks' right factors at once: block 1 over all
+// 32 rows, block 0 over rows 0..15 (half a tile), next to the left factors.
+constexpr int factor_bytes(int ref) { return ref == 16 ? 7 * kTileA : kFactorBytes; }
 constexpr int gref_bytes(int ref) { return (32 / ref + 1) * 128 * 4; }
 constexpr int off_x(int ref) { return (kOffGref + gref_bytes(ref) + 255) / 256 * 256; }
 constexpr int lds_bytes(int ref) {
-  return off_x(ref) + (kFactorBytes > kProductBytes ? kFactorBytes : kProductBytes);
+  return off_x(ref) + (factor_bytes(ref) > kProductBytes ? factor_bytes(ref) : kProductBytes);
 }
-static_assert(lds_bytes(16) <= 80 * 1024, "two workgroups per CU at the default block");
+static_assert(2 * lds_bytes(16) <= 160 * 1024, "two workgroups per CU at the default block");
 
 // Offsets inside region X.
 constexpr int xLKh = 0, xLKl = xLKh + kTileA, xLQh = xLKl + kTileA, xLQl = xLQh + kTileA, xRh = xLQl + kTileA,
               xRl = xRh + kTileA;
+// REF = 16: R of block 1 at xRh / xRl (32 rows), R of block 0 (16 rows each) after them.
+constexpr int xR0h = xRl + kTileA, xR0l = xR0h + kTileA / 2;
 constexpr int xKGh = 0, xKGl = xKGh + kTileT, xKt = xKGl + kTileT, xVt = xKt + kTileT, xQs = xVt + kTileT,
               xTh = xQs + kTileA, xTl = xTh + kTileTT;
 
@@ -277,6 +283,62 @@ __device__ void process_item(const Plan& p, const Item& it, const Inputs& in, ch
   const int jt = (w < 2) ? w : 1;
   const int ja = (w < 2) ? 0 : 1;
   f32x4 acc[2] = {zero4(), zero4()};
+  if constexpr (REF == 16) {
+    // Both row blocks at once. Row tile t is exactly row block t (reference row 16t),
+    // so every job's rows are inside its block and no row masking is needed. Right
+    // factors: block 1 over all rows (k_i e^{G_16 - G_i}), block 0 over rows 0..15
+    // (k_i e^{G_0 - G_i}); the exponent is minus the left factor's for the rows of the
+    // factor's own block, and for block 1 on rows 0..15 it is block 0's plus G_16 - G_0.
+    {
+      const float2 g0 = *reinterpret_cast<const float2*>(Gref + c0);
+      const float2 g16 = *reinterpret_cast<const float2*>(Gref + 128 + c0);
+      const float d0 = __expf(g16.x - g0.x), d1 = __expf(g16.y - g0.y);  // e^{G_16 - G_0} <= 1
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int r = 8 * w + i;
+        const float2 gm = (r < 16) ? g0 : g16;
+        const float r0 = __expf(gm.x - G[i][0]), r1 = __expf(gm.y - G[i][1]);  // own block, <= e^80
+        __bf16 h0, l0, h1, l1;
+        const int o = (r * LDA + c0) * 2;
+        if (r < 16) {
+          split_bf16(kn[i][0] * r0, h0, l0);
+          split_bf16(kn[i][1] * r1, h1, l1);
+          *reinterpret_cast<uint32_t*>(X + xR0h + o) = pack2(h0, h1);
+          *reinterpret_cast<uint32_t*>(X + xR0l + o) = pack2(l0, l1);
+          split_bf16(kn[i][0] * (r0 * d0), h0, l0);  // e^{G_16 - G_r} <= 1
+          split_bf16(kn[i][1] * (r1 * d1), h1, l1);
+        } else {
+          split_bf16(kn[i][0] * r0, h0, l0);
+          split_bf16(kn[i][1] * r1, h1, l1);
+        }
+        *reinterpret_cast<uint32_t*>(X + xRh + o) = pack2(h0, h1);
+        *reinterpret_cast<uint32_t*>(X + xRl + o) = pack2(l0, l1);
+      }
+    }
+    __syncthreads();
+    {
+      const int row = 16 * jt + l16;
+      const int col = 16 * ja + l16;
+      const int rb_h = (jt == 0) ? xR0h : xRh;  // right factors of the row tile's block
+      const int rb_l = (jt == 0) ? xR0l : xRl;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int ea = (row * LDA + 32 * kk + 8 * g4) * 2;
+        const int eb = (col * LDA + 32 * kk + 8 * g4) * 2;
+        const bf16x8 bh = ld_frag(X, rb_h + eb), bl = ld_frag(X, rb_l + eb);
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb) {
+          if (jb >= njobs) break;
+          const int mat = (w < 2) ? jb : (w - 2);
+          const bf16x8 ah = ld_frag(X, (mat ? xLQh : xLKh) + ea), al = ld_frag(X, (mat ? xLQl : xLKl) + ea);
+          acc[jb] = mfma(ah, bh, acc[jb]);
+          acc[jb] = mfma(ah, bl, acc[jb]);
+          acc[jb] = mfma(al, bh, acc[jb]);
+        }
+      }
+    }
+    __syncthreads();
+  } else
   for (int b = 0; b < NB; ++b) {
     const int mb = b * REF;
     const int lim = mb + REF - 1;  // last row of the block: right factors beyond it are 0
@@ -376,7 +438,7 @@ __device__ void process_item(const Plan& p, const Item& it, const Inputs& in, ch
   }
   __syncthreads();
 
-  // ---------------------------------------------------------------- solve (part 1) + stores
+  // ---------------------------------------------------------------- solve + stores
   if (w == 0) {
     if (lane < 32) {
       // Diagonal 16x16 blocks of T = (I + A)^{-1}: lane -> (block, column j). Forward
@@ -400,6 +462,26 @@ __device__ void process_item(const Plan& p, const Item& it, const Inputs& in, ch
 #pragma unroll
       for (int i = 0; i < 16; ++i) Ts[(base + i) * LDF + base + j] = tc[i];
     }
+    // Off-diagonal block T10 = -T11 (A10 T00) on fp32 MFMA (16x16x4: lane l holds A[l%16]
+    // [l/16] and B[l/16][l%16], D rows 4*(l/16) + i of column l%16). The diagonal blocks
+    // were written by lanes 0..31 of this wave: wait for those LDS writes, and keep the
+    // compiler from moving LDS accesses across the wait (the lanes exchange data).
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    f32x4 m = zero4();
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4)
+      m = __builtin_amdgcn_mfma_f32_16x16x4f32(As[(16 + l16) * LDF + 4 * s4 + g4], Ts[(4 * s4 + g4) * LDF + l16], m,
+                                               0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) Ms[(4 * g4 + i) * LDF + l16] = m[i];
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    f32x4 t10 = zero4();
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4)
+      t10 = __builtin_amdgcn_mfma_f32_16x16x4f32(Ts[(16 + l16) * LDF + 16 + 4 * s4 + g4], Ms[(4 * s4 + g4) * LDF + l16],
+                                                 t10, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) Ts[(16 + 4 * g4 + i) * LDF + l16] = -t10[i];
   } else {
     // 18 fragments (Q: 8, K: 8, P: 2), six per wave.
     for (int f = (w - 1) * 6; f < w * 6; ++f) {
@@ -427,22 +509,6 @@ __device__ void process_item(const Plan& p, const Item& it, const Inputs& in, ch
       }
       *reinterpret_cast<bf16x8*>(rec + dst + lane * 16) = val;
     }
-  }
-  __syncthreads();
-  // ---------------------------------------------------------------- solve (part 2)
-  // Off-diagonal block: T10 = -T11 A10 T00, one 16x16 output element per thread.
-  {
-    const int i = tid >> 4, j = tid & 15;
-    float m = 0.f;
-    for (int k = j; k < 16; ++k) m = fmaf(As[(16 + i) * LDF + k], Ts[k * LDF + j], m);  // (A10 T00)[i][j]
-    Ms[i * LDF + j] = m;
-  }
-  __syncthreads();
-  {
-    const int i = tid >> 4, j = tid & 15;
-    float t = 0.f;
-    for (int k = 0; k <= i; ++k) t = fmaf(Ts[(16 + i) * LDF + 16 + k], Ms[k * LDF + j], t);
-    Ts[(16 + i) * LDF + j] = -t;
   }
   __syncthreads();
   // T diag(beta) as hi/lo bf16 (rows r, column r'), zero above the diagonal.
