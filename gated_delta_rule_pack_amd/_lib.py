@@ -72,7 +72,7 @@ EVREC = CFUNCTYPE(c_int, c_void_p, c_void_p, c_void_p)
 WAIT = CFUNCTYPE(c_int, c_void_p, c_void_p, c_void_p)
 ALLOC = CFUNCTYPE(c_int, c_void_p, POINTER(c_void_p), c_size_t)
 FREE = CFUNCTYPE(c_int, c_void_p, c_void_p)
-LAUNCH = CFUNCTYPE(c_int, c_void_p, c_int, c_void_p, c_void_p)
+LAUNCH = CFUNCTYPE(c_int, c_void_p, c_int, c_void_p, c_void_p, c_void_p, c_void_p)
 ELAPSED = CFUNCTYPE(c_int, c_void_p, POINTER(c_float), c_void_p, c_void_p)
 
 
@@ -87,6 +87,7 @@ class Runtime(Structure):
         ("device_alloc", ALLOC), ("device_free", FREE),
         ("launch", LAUNCH),
         ("event_create_timed", EVCREATE), ("event_elapsed_ms", ELAPSED),
+        ("event_create_completion", EVCREATE),
     ]
 
 

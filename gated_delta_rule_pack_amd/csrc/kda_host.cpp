@@ -61,16 +61,24 @@ int rt_host_alloc(void*, void** p, size_t n) { return (int)hipHostMalloc(p, n, h
 int rt_host_free(void*, void* p) { return (int)hipHostFree(p); }
 int rt_dev_alloc(void*, void** p, size_t n) { return (int)hipMalloc(p, n); }
 int rt_dev_free(void*, void* p) { return (int)hipFree(p); }
-int rt_launch(void*, int kernel, const void* plan, void* s) {
+int rt_launch(void*, int kernel, const void* plan, void* s, void* start, void* stop) {
   const kda::Plan& p = *reinterpret_cast<const kda::Plan*>(plan);
   switch (kernel) {
-    case 0: return kda::launch_prep(p, s);
-    case 1: return kda::launch_scan(p, s);
-    case 2: return kda::launch_segmap(p, s);
-    default: return kda::launch_segcombine(p, s);
+    case 0: return kda::launch_prep(p, s, start, stop);
+    case 1: return kda::launch_scan(p, s, start, stop);
+    case 2: return kda::launch_segmap(p, s, start, stop);
+    default: return kda::launch_segcombine(p, s, start, stop);
   }
 }
-int rt_ev_create_timed(void*, void** ev) { return (int)hipEventCreate(reinterpret_cast<hipEvent_t*>(ev)); }
+// Timing and completion-only events skip the system-scope fence: nothing the host reads
+// depends on them, and the fence's cache write-back would idle the GPU between calls.
+int rt_ev_create_timed(void*, void** ev) {
+  return (int)hipEventCreateWithFlags(reinterpret_cast<hipEvent_t*>(ev), hipEventDisableSystemFence);
+}
+int rt_ev_create_completion(void*, void** ev) {
+  return (int)hipEventCreateWithFlags(reinterpret_cast<hipEvent_t*>(ev),
+                                      hipEventDisableTiming | hipEventDisableSystemFence);
+}
 int rt_ev_elapsed(void*, float* ms, void* a, void* b) {
   return (int)hipEventElapsedTime(ms, (hipEvent_t)a, (hipEvent_t)b);
 }
@@ -78,7 +86,7 @@ int rt_ev_elapsed(void*, float* ms, void* a, void* b) {
 const kda_runtime kHipRuntime = {nullptr,    rt_h2d,        rt_d2h,         rt_sync,     rt_capturing,
                                  rt_ev_create, rt_ev_destroy, rt_ev_record, rt_ev_query, rt_ev_sync,
                                  rt_wait,    rt_host_alloc, rt_host_free,   rt_dev_alloc, rt_dev_free,
-                                 rt_launch,  rt_ev_create_timed, rt_ev_elapsed};
+                                 rt_launch,  rt_ev_create_timed, rt_ev_elapsed, rt_ev_create_completion};
 
 // ------------------------------------------------------------------ metadata
 inline size_t align4(size_t n) { return (n + 3) & ~size_t(3); }  // int32 count -> 16-byte blocks
@@ -250,7 +258,8 @@ struct Graveyard {
 };
 
 struct ProfileMarks {
-  void* ev[3];  // before prep, between prep and scan, after scan
+  void* ev[4];        // prep start, prep end, scan phase start (segment kernels or scan), scan end
+  bool prep = false;  // the call launched prep
 };
 
 struct kda_ctx {
@@ -320,19 +329,24 @@ void evict_one(kda_ctx* ctx) {
   delete e;
 }
 
-kda_status record_use(kda_ctx* ctx, CacheEntry* e, void* stream) {
+// The completion event that tracks this entry's last use on a stream (created on the first
+// use there). The call's last kernel records it on completion, so an evicted buffer is
+// freed only after every launch that read it has finished.
+kda_status use_event(kda_ctx* ctx, CacheEntry* e, void* stream, void** ev) {
   for (auto& u : e->uses)
-    if (u.first == stream) return ctx->rt.event_record(ctx->rt.user, u.second, stream) ? hip_fail() : KDA_OK;
-  void* ev = nullptr;
-  if (ctx->rt.event_create(ctx->rt.user, &ev)) return hip_fail();
-  if (ctx->rt.event_record(ctx->rt.user, ev, stream)) return hip_fail();
-  e->uses.push_back({stream, ev});
+    if (u.first == stream) {
+      *ev = u.second;
+      return KDA_OK;
+    }
+  if (ctx->rt.event_create_completion(ctx->rt.user, ev)) return hip_fail();
+  e->uses.push_back({stream, *ev});
   return KDA_OK;
 }
 
 // Find or upload the metadata for these bounds.
-kda_status get_meta(kda_ctx* ctx, const int32_t* cu, int N, int seg_len, void* stream, CacheEntry** out) {
-  int capturing = 0;
+kda_status get_meta(kda_ctx* ctx, const int32_t* cu, int N, int seg_len, void* stream, CacheEntry** out,
+                    int& capturing) {
+  capturing = 0;
   if (ctx->rt.stream_is_capturing(ctx->rt.user, stream, &capturing)) return hip_fail();
   const uint64_t hsh = hash_bounds(cu, N);
   for (CacheEntry* e : ctx->cache) {
@@ -635,7 +649,8 @@ kda_status kda_chunk_fwd(kda_ctx* ctx, const kda_fwd_args* a, void* ws, size_t w
   int seg_len = seg_len_for(a->N, a->H, max_seq_chunks(cu, a->N));
   if (ctx->seg_len_override >= 0 && (int64_t)a->N * a->H <= 96) seg_len = ctx->seg_len_override;
   CacheEntry* e = nullptr;
-  st = get_meta(ctx, cu, a->N, seg_len, stream, &e);
+  int capturing = 0;
+  st = get_meta(ctx, cu, a->N, seg_len, stream, &e, capturing);
   if (st != KDA_OK) return st;
   const WsLayout wl = ws_layout(a);
 
@@ -689,28 +704,33 @@ kda_status kda_chunk_fwd(kda_ctx* ctx, const kda_fwd_args* a, void* ws, size_t w
   p.starts = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + wl.starts);
   p.cu_count = ctx->cu_count;
 
+  // Launches. Under capture the entry is retained (never evicted), so no completion event
+  // is attached, and no timing events are recorded.
+  const bool prof = ctx->profiling && !capturing;
+  void* use_ev = nullptr;
+  if (!capturing && (st = use_event(ctx, e, stream, &use_ev)) != KDA_OK) return st;
   ProfileMarks pm{};
-  if (ctx->profiling) {
+  if (prof) {
     if (!ctx->marks_free.empty()) {
       pm = ctx->marks_free.back();
       ctx->marks_free.pop_back();
     } else {
-      for (void*& e : pm.ev)
-        if (rt.event_create_timed(rt.user, &e)) return hip_fail();
+      for (void*& ev : pm.ev)
+        if (rt.event_create_timed(rt.user, &ev)) return hip_fail();
     }
-    ctx->marks.push_back(pm);
-    if (rt.event_record(rt.user, pm.ev[0], stream)) return hip_fail();
+    pm.prep = p.n_chunks > 0;
   }
-  if (rt.launch(rt.user, 0, &p, stream)) return hip_fail();
-  if (ctx->profiling && rt.event_record(rt.user, pm.ev[1], stream)) return hip_fail();
+  if (p.n_chunks > 0 && rt.launch(rt.user, 0, &p, stream, pm.ev[0], pm.ev[1])) return hip_fail();
   if (p.n_maps > 0) {
-    if (rt.launch(rt.user, 2, &p, stream)) return hip_fail();
-    if (rt.launch(rt.user, 3, &p, stream)) return hip_fail();
+    if (rt.launch(rt.user, 2, &p, stream, pm.ev[2], nullptr)) return hip_fail();
+    if (rt.launch(rt.user, 3, &p, stream, nullptr, nullptr)) return hip_fail();
   }
-  if (rt.launch(rt.user, 1, &p, stream)) return hip_fail();
-  if (ctx->profiling && rt.event_record(rt.user, pm.ev[2], stream)) return hip_fail();
-  st = record_use(ctx, e, stream);
-  if (st != KDA_OK) return st;
+  if (rt.launch(rt.user, 1, &p, stream, p.n_maps > 0 ? nullptr : pm.ev[2], prof ? pm.ev[3] : use_ev))
+    return hip_fail();
+  if (prof) {
+    ctx->marks.push_back(pm);
+    if (use_ev && rt.event_record(rt.user, use_ev, stream)) return hip_fail();
+  }
   ctx->stats.calls++;
   ctx->stats.last_dv_split = p.dv_split;
   ctx->stats.last_ref_block = p.ref_block;
@@ -731,9 +751,9 @@ kda_status kda_profile_read(kda_ctx* ctx, double* prep_ms, double* scan_ms, int6
   auto& rt = ctx->rt;
   double a = 0.0, b = 0.0;
   for (auto& m : ctx->marks) {
-    if (rt.event_synchronize(rt.user, m.ev[2])) return hip_fail();
+    if (rt.event_synchronize(rt.user, m.ev[3])) return hip_fail();
     float x = 0.f, y = 0.f;
-    if (rt.event_elapsed_ms(rt.user, &x, m.ev[0], m.ev[1]) || rt.event_elapsed_ms(rt.user, &y, m.ev[1], m.ev[2]))
+    if ((m.prep && rt.event_elapsed_ms(rt.user, &x, m.ev[0], m.ev[1])) || rt.event_elapsed_ms(rt.user, &y, m.ev[2], m.ev[3]))
       return hip_fail();
     a += x;
     b += y;

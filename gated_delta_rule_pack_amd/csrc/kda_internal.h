@@ -82,9 +82,13 @@ struct Plan {
 };
 
 // Launchers (defined in the .hip files). Return 0 on success, nonzero HIP error code.
-int launch_prep(const Plan& p, void* stream);
-int launch_scan(const Plan& p, void* stream);
-int launch_segmap(const Plan& p, void* stream);
-int launch_segcombine(const Plan& p, void* stream);
+// start / stop, when not null, are HIP events the launch itself records when the kernel
+// starts and when it completes (no separate marker in the stream). Each launcher is
+// called only when its kernel has work: prep when n_chunks > 0, the segment kernels when
+// n_maps > 0; the scan always has at least one (segment, head) unit.
+int launch_prep(const Plan& p, void* stream, void* start, void* stop);
+int launch_scan(const Plan& p, void* stream, void* start, void* stop);
+int launch_segmap(const Plan& p, void* stream, void* start, void* stop);
+int launch_segcombine(const Plan& p, void* stream, void* start, void* stop);
 
 }  // namespace kda

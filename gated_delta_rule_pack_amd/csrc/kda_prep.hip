@@ -29,6 +29,7 @@
 // cumsum is mostly in registers and transposed tiles are written 16 bytes at a time.
 // Output: one record per (head, chunk) in the scan's MFMA fragment order.
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include "kda_device.h"
@@ -594,7 +595,7 @@ __global__ __launch_bounds__(kThreadsPrep, 2) void prep_kernel(Plan p, int n_ite
 }
 
 template <int REF>
-int launch_ref(const Plan& p, hipStream_t s, int grid) {
+int launch_ref(const Plan& p, hipStream_t s, int grid, hipEvent_t start, hipEvent_t stop) {
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prep_kernel<REF>),
@@ -603,22 +604,24 @@ int launch_ref(const Plan& p, hipStream_t s, int grid) {
     attr_set = true;
   }
   const int n_items = p.n_chunks * p.H;
-  hipLaunchKernelGGL(prep_kernel<REF>, dim3(min(grid, n_items)), dim3(kThreadsPrep), lds_bytes(REF), s, p, n_items);
+  hipExtLaunchKernelGGL(prep_kernel<REF>, dim3(min(grid, n_items)), dim3(kThreadsPrep), lds_bytes(REF), s, start, stop,
+                        0, p, n_items);
   return (int)hipGetLastError();
 }
 
 }  // namespace
 
-int launch_prep(const Plan& p, void* stream) {
-  if (p.n_chunks == 0) return 0;
+int launch_prep(const Plan& p, void* stream, void* start, void* stop) {
+  if (p.n_chunks == 0) return (int)hipErrorInvalidValue;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipEvent_t e0 = reinterpret_cast<hipEvent_t>(start), e1 = reinterpret_cast<hipEvent_t>(stop);
   const int grid = 2 * p.cu_count;  // persistent: two resident workgroups per CU
   switch (p.ref_block) {
-    case 16: return launch_ref<16>(p, s, grid);
-    case 8: return launch_ref<8>(p, s, grid);
-    case 4: return launch_ref<4>(p, s, grid);
-    case 2: return launch_ref<2>(p, s, grid);
-    default: return launch_ref<1>(p, s, grid);
+    case 16: return launch_ref<16>(p, s, grid, e0, e1);
+    case 8: return launch_ref<8>(p, s, grid, e0, e1);
+    case 4: return launch_ref<4>(p, s, grid, e0, e1);
+    case 2: return launch_ref<2>(p, s, grid, e0, e1);
+    default: return launch_ref<1>(p, s, grid, e0, e1);
   }
 }
 

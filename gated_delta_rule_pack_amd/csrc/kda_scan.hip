@@ -32,6 +32,7 @@
 // chunk's U (they end as the state C the segment reaches from zero); one workgroup per
 // half.
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include "kda_device.h"
@@ -650,7 +651,7 @@ int set_lds_limit(KernelT* kernel, size_t bytes, bool& done) {
 }
 
 template <int NTW, int SDT>
-int launch_scan_ntw(const Plan& p, hipStream_t s) {
+int launch_scan_ntw(const Plan& p, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   constexpr size_t bytes = HeadLds<NTW>::kBytes;
   static_assert(bytes <= 160 * 1024, "fits one CU's LDS");
   static bool done = false;
@@ -658,12 +659,13 @@ int launch_scan_ntw(const Plan& p, hipStream_t s) {
   const int groups = 2 / NTW;  // value-channel halves per (segment, head)
   const int units = p.n_seg * p.H;
   const int nblocks = 8 * ((units + 7) / 8) * groups;
-  hipLaunchKernelGGL((head_kernel<NTW, SDT, kKernelScan>), dim3(nblocks), dim3(320), bytes, s, p, units, groups);
+  hipExtLaunchKernelGGL((head_kernel<NTW, SDT, kKernelScan>), dim3(nblocks), dim3(320), bytes, s, e0, e1, 0, p, units,
+                        groups);
   return (int)hipGetLastError();
 }
 
 template <int NT, int SDT>
-int launch_narrow(const Plan& p, hipStream_t s) {
+int launch_narrow(const Plan& p, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   constexpr int R = 5;                 // ring slots: the loader runs 4 chunks ahead
   constexpr int DO = NT == 1 ? 4 : 3;  // output-wave fragment depth
   constexpr size_t bytes = NarrowLds<NT, R>::kBytes;
@@ -673,40 +675,42 @@ int launch_narrow(const Plan& p, hipStream_t s) {
   const int groups = 8 / NT;
   const int units = p.n_seg * p.H;
   const int nblocks = 8 * ((units + 7) / 8) * groups;
-  hipLaunchKernelGGL((scan_narrow<NT, SDT, R, DO>), dim3(nblocks), dim3(256), bytes, s, p, units, groups);
+  hipExtLaunchKernelGGL((scan_narrow<NT, SDT, R, DO>), dim3(nblocks), dim3(256), bytes, s, e0, e1, 0, p, units, groups);
   return (int)hipGetLastError();
 }
 
 template <int SDT>
-int launch_scan_dt(const Plan& p, hipStream_t s) {
+int launch_scan_dt(const Plan& p, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   switch (p.dv_split) {
-    case 8: return launch_narrow<1, SDT>(p, s);
-    case 4: return launch_narrow<2, SDT>(p, s);
-    case 2: return launch_scan_ntw<1, SDT>(p, s);
-    default: return launch_scan_ntw<2, SDT>(p, s);
+    case 8: return launch_narrow<1, SDT>(p, s, e0, e1);
+    case 4: return launch_narrow<2, SDT>(p, s, e0, e1);
+    case 2: return launch_scan_ntw<1, SDT>(p, s, e0, e1);
+    default: return launch_scan_ntw<2, SDT>(p, s, e0, e1);
   }
 }
 
 }  // namespace
 
-int launch_scan(const Plan& p, void* stream) {
+int launch_scan(const Plan& p, void* stream, void* start, void* stop) {
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipEvent_t e0 = reinterpret_cast<hipEvent_t>(start), e1 = reinterpret_cast<hipEvent_t>(stop);
   switch (p.state_dtype) {
-    case kF16: return launch_scan_dt<kF16>(p, s);
-    case kBF16: return launch_scan_dt<kBF16>(p, s);
-    default: return launch_scan_dt<kF32>(p, s);
+    case kF16: return launch_scan_dt<kF16>(p, s, e0, e1);
+    case kBF16: return launch_scan_dt<kBF16>(p, s, e0, e1);
+    default: return launch_scan_dt<kF32>(p, s, e0, e1);
   }
 }
 
-int launch_segmap(const Plan& p, void* stream) {
-  if (p.n_maps == 0) return 0;
+int launch_segmap(const Plan& p, void* stream, void* start, void* stop) {
+  if (p.n_maps == 0) return (int)hipErrorInvalidValue;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipEvent_t e0 = reinterpret_cast<hipEvent_t>(start), e1 = reinterpret_cast<hipEvent_t>(stop);
   constexpr size_t bytes = HeadLds<2>::kBytes;
   static bool done = false;
   if (int e = set_lds_limit(&head_kernel<2, kF32, kKernelMap>, bytes, done)) return e;
   const int units = p.n_maps * p.H;
   const int nblocks = 8 * ((units + 7) / 8) * 2;  // halves A and C
-  hipLaunchKernelGGL((head_kernel<2, kF32, kKernelMap>), dim3(nblocks), dim3(320), bytes, s, p, units, 2);
+  hipExtLaunchKernelGGL((head_kernel<2, kF32, kKernelMap>), dim3(nblocks), dim3(320), bytes, s, e0, e1, 0, p, units, 2);
   return (int)hipGetLastError();
 }
 

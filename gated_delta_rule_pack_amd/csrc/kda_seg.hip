@@ -15,6 +15,7 @@
 // from the call's initial state, in fp32 (bf16 hi/lo operand splits on MFMA), and stores
 // the results: the start states the scan runs the segments from.
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include "kda_device.h"
@@ -142,14 +143,15 @@ __global__ __launch_bounds__(256) void segcombine_kernel(Plan p) {
 
 }  // namespace
 
-int launch_segcombine(const Plan& p, void* stream) {
-  if (p.n_multi == 0) return 0;
+int launch_segcombine(const Plan& p, void* stream, void* start, void* stop) {
+  if (p.n_multi == 0) return (int)hipErrorInvalidValue;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipEvent_t e0 = reinterpret_cast<hipEvent_t>(start), e1 = reinterpret_cast<hipEvent_t>(stop);
   const dim3 grid(p.n_multi * p.H * 4);
   switch (p.state_dtype) {
-    case kF16: hipLaunchKernelGGL(segcombine_kernel<kF16>, grid, dim3(256), 0, s, p); break;
-    case kBF16: hipLaunchKernelGGL(segcombine_kernel<kBF16>, grid, dim3(256), 0, s, p); break;
-    default: hipLaunchKernelGGL(segcombine_kernel<kF32>, grid, dim3(256), 0, s, p); break;
+    case kF16: hipExtLaunchKernelGGL(segcombine_kernel<kF16>, grid, dim3(256), 0, s, e0, e1, 0, p); break;
+    case kBF16: hipExtLaunchKernelGGL(segcombine_kernel<kBF16>, grid, dim3(256), 0, s, e0, e1, 0, p); break;
+    default: hipExtLaunchKernelGGL(segcombine_kernel<kF32>, grid, dim3(256), 0, s, e0, e1, 0, p); break;
   }
   return (int)hipGetLastError();
 }

@@ -142,13 +142,18 @@ typedef struct kda_runtime {
   int (*host_free_pinned)(void* user, void* ptr);
   int (*device_alloc)(void* user, void** ptr, size_t bytes);
   int (*device_free)(void* user, void* ptr);
-  /* kernel: 0 = prep, 1 = scan, 2 = segment maps, 3 = segment combine (2 and 3 only
-   * for a segmented call, between prep and scan). plan is internal launch data, opaque
-   * to the runtime. */
-  int (*launch)(void* user, int kernel, const void* plan, void* stream);
+  /* kernel: 0 = prep (only when the call has chunks), 1 = scan, 2 = segment maps,
+   * 3 = segment combine (2 and 3 only for a segmented call, between prep and scan). plan
+   * is internal launch data, opaque to the runtime. start and stop, when not NULL, are
+   * events the launch itself records when the kernel starts and when it completes
+   * (hipExtLaunchKernel), with no separate marker in the stream. */
+  int (*launch)(void* user, int kernel, const void* plan, void* stream, void* start, void* stop);
   /* Timing events (used only while profiling is enabled). */
   int (*event_create_timed)(void* user, void** event);
   int (*event_elapsed_ms)(void* user, float* ms, void* start, void* end);
+  /* Completion events: they only tell the host that a launch has finished (they track the
+   * last use of a cached metadata buffer) and carry no memory fence. */
+  int (*event_create_completion)(void* user, void** event);
 } kda_runtime;
 
 /* Context: device properties (CU count), pinned staging ring, metadata cache, stats.

@@ -223,6 +223,7 @@ class FakeRuntime:
         self.alloc = {}
         self.uploads = []
         self.launches = []
+        self.launch_events = []
         rt = _lib.Runtime()
         rt.user = None
         self._cbs = dict(
@@ -234,7 +235,7 @@ class FakeRuntime:
             host_alloc_pinned=_lib.ALLOC(self._halloc), host_free_pinned=_lib.FREE(self._hfree),
             device_alloc=_lib.ALLOC(self._dalloc), device_free=_lib.FREE(self._dfree),
             launch=_lib.LAUNCH(self._launch), event_create_timed=_lib.EVCREATE(self._ev_create),
-            event_elapsed_ms=_lib.ELAPSED(self._elapsed))
+            event_elapsed_ms=_lib.ELAPSED(self._elapsed), event_create_completion=_lib.EVCREATE(self._ev_create))
         for k, v in self._cbs.items():
             setattr(rt, k, v)
         self.rt = rt
@@ -307,8 +308,14 @@ class FakeRuntime:
         self.log.append(("dev_free", p))
         return 0
 
-    def _launch(self, user, k, plan, s):
+    def _launch(self, user, k, plan, s, start, stop):
+        # Events attached to a launch are recorded by it, as a marker right after it would be.
         self.launches.append((k, s))
+        self.launch_events.append((k, start or 0, stop or 0))
+        for e in (start, stop):
+            if e:
+                self.pending.add(e)
+                self.log.append(("record", e, s))
         return 0
 
     def _elapsed(self, user, out, a, b):
@@ -371,6 +378,47 @@ def test_host_bounds_issue_no_sync_and_one_upload(lib, fake):
     assert fake.syncs() == []
     st = _stats(lib, fake)
     assert st["cache_hits"] == 1 and st["calls"] == 2 and st["last_n_chunks"] == 11
+
+
+def test_hit_path_records_only_the_launch_attached_completion(lib, fake):
+    """On a cache hit the only stream operations are the two launches: the entry's use is
+    tracked by a completion event the scan launch records itself, the same event on every
+    call on one stream, with no marker of its own."""
+    bufs = FakeBufs()
+    a, _, _ = _valid_args(bufs, T=300, N=4, cu=np.array([0, 0, 100, 100, 300], np.int32), paged=True)
+    assert _call(lib, fake, a) == _lib.KDA_OK
+    mark = len(fake.log)
+    for _ in range(3):
+        assert _call(lib, fake, a) == _lib.KDA_OK
+    ev = fake.launch_events[1][2]
+    assert ev != 0 and fake.launch_events[0] == (0, 0, 0)
+    assert fake.launch_events[2:] == [(0, 0, 0), (1, 0, ev)] * 3
+    assert fake.log[mark:] == [("record", ev, 0x10)] * 3
+    # A second stream gets its own completion event.
+    assert _call(lib, fake, a, stream=0x20) == _lib.KDA_OK
+    ev2 = fake.launch_events[-1][2]
+    assert fake.launch_events[-1][0] == 1 and ev2 not in (0, ev)
+
+
+def test_profiling_attaches_timing_events_to_launches(lib, fake):
+    """While profiling, prep and scan carry start / end timing events; the use event is then
+    recorded after the scan. A call without chunks launches the scan alone and reads back
+    a zero prep time."""
+    bufs = FakeBufs()
+    a, _, _ = _valid_args(bufs, T=300, N=4, cu=np.array([0, 0, 100, 100, 300], np.int32), paged=True)
+    assert lib.kda_profile_enable(fake.ctx, 1) == _lib.KDA_OK
+    assert _call(lib, fake, a) == _lib.KDA_OK
+    (k0, s0, e0), (k1, s1, e1) = fake.launch_events
+    assert (k0, k1) == (0, 1) and len({s0, e0, s1, e1}) == 4 and 0 not in (s0, e0, s1, e1)
+    assert fake.log[-1][0] == "record" and fake.log[-1][1] not in (s0, e0, s1, e1)
+    b, _, _ = _valid_args(bufs, T=0, N=2, cu=np.array([0, 0, 0], np.int32), paged=True)
+    fake.launches.clear()
+    assert _call(lib, fake, b) == _lib.KDA_OK
+    assert fake.launches == [(1, 0x10)]
+    prep, scan, calls = ctypes.c_double(), ctypes.c_double(), ctypes.c_int64()
+    assert lib.kda_profile_read(fake.ctx, ctypes.byref(prep), ctypes.byref(scan), ctypes.byref(calls)) == _lib.KDA_OK
+    assert calls.value == 2 and prep.value == 1.0 and scan.value == 2.0
+    assert lib.kda_profile_enable(fake.ctx, 0) == _lib.KDA_OK
 
 
 def _segments_reference(cu, L):
