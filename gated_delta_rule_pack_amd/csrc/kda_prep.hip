@@ -102,17 +102,18 @@ __device__ __forceinline__ Item item_of(const Plan& p, int item) {
 __device__ __forceinline__ void load_inputs(const Plan& p, const Item& it, int w, int lane, Inputs& in) {
   const int H = p.H;
   const int last = p.T - 1;
+  // Row pointers are uniform (scalar); the lane's channel pair is a 32-bit offset.
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int row = min(it.t0 + 8 * w + i, last);
-    const size_t e = ((size_t)row * H + it.h) * kHead + 2 * lane;
-    in.q[i] = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint16_t*>(p.q) + e);
-    in.k[i] = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint16_t*>(p.k) + e);
-    in.v[i] = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint16_t*>(p.v) + e);
+    const size_t e = ((size_t)row * H + it.h) * kHead;
+    in.q[i] = reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint16_t*>(p.q) + e)[lane];
+    in.k[i] = reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint16_t*>(p.k) + e)[lane];
+    in.v[i] = reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint16_t*>(p.v) + e)[lane];
     if (p.g_dtype == kF32) {
-      in.g[i] = *reinterpret_cast<const float2*>(reinterpret_cast<const float*>(p.g_raw) + e);
+      in.g[i] = reinterpret_cast<const float2*>(reinterpret_cast<const float*>(p.g_raw) + e)[lane];
     } else {
-      const uint32_t b = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint16_t*>(p.g_raw) + e);
+      const uint32_t b = reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint16_t*>(p.g_raw) + e)[lane];
       in.g[i] = make_float2(__uint_as_float(b << 16), __uint_as_float(b & 0xffff0000u));
     }
   }
@@ -125,10 +126,23 @@ __device__ __forceinline__ void load_inputs(const Plan& p, const Item& it, int w
 __device__ __forceinline__ float lo16(uint32_t x) { return __uint_as_float(x << 16); }
 __device__ __forceinline__ float hi16(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
 __device__ __forceinline__ float rcp(float x) { return __builtin_amdgcn_rcpf(x); }
-__device__ __forceinline__ float sigm(float x) { return rcp(1.0f + __expf(-x)); }
+// The gate cumsum is kept in base 2 (G2 = G log2 e), so every decay factor e^{G_a - G_b}
+// is one subtraction and the hardware's 2^x. Its results below the fp32 normal range
+// may flush to zero, which only drops terms smaller than 2^-126 of their sum.
+constexpr float kLog2e = 1.4426950408889634f;
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float sigm(float x) { return rcp(1.0f + ex2(-kLog2e * x)); }
 
-__device__ __forceinline__ uint32_t pack2(__bf16 a, __bf16 b) {
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+// Two floats to packed bf16 (round to nearest even; a in the low half).
+__device__ __forceinline__ uint32_t cvt_pk(float a, float b) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
+}
+// Two floats split into packed bf16 hi and lo words, x = hi + lo to about 2^-17 |x|.
+__device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t& lo) {
+  hi = cvt_pk(a, b);
+  lo = cvt_pk(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xffff0000u));
 }
 
 __device__ __forceinline__ bf16x8 ld_frag(const char* lds, int off) {
@@ -142,14 +156,10 @@ __device__ __forceinline__ bf16x8 ld_frag_2x4(const char* lds, int off0, int off
   return __builtin_bit_cast(bf16x8, r);
 }
 
-// Write 8 bf16 (one channel, rows 8w .. 8w+7) to a transposed [128][LDT] tile.
-__device__ __forceinline__ void st_col8(char* lds, int off, int c, int w, const __bf16* v) {
-  uint4 x;
-  x.x = pack2(v[0], v[1]);
-  x.y = pack2(v[2], v[3]);
-  x.z = pack2(v[4], v[5]);
-  x.w = pack2(v[6], v[7]);
-  *reinterpret_cast<uint4*>(lds + off + (c * LDT + 8 * w) * 2) = x;
+// Write 8 bf16 (one channel, rows 8w .. 8w+7, packed two rows a word) to a transposed
+// [128][LDT] tile.
+__device__ __forceinline__ void st_col8(char* lds, int off, int c, int w, const uint32_t* v) {
+  *reinterpret_cast<uint4*>(lds + off + (c * LDT + 8 * w) * 2) = uint4{v[0], v[1], v[2], v[3]};
 }
 
 // Sum 16 per-lane values over the 64 lanes of a wave with 17 exchanges: each step keeps
@@ -220,18 +230,20 @@ __device__ void process_item(const Plan& p, const Item& it, const Inputs& in, ch
     const float s = wave_sum16(sq, lane);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float rq = rsqrtf(__shfl(s, lane_of_sum(i)) + 1e-6f);
-      const float rk = rsqrtf(__shfl(s, lane_of_sum(8 + i)) + 1e-6f);
+      const float rq = __builtin_amdgcn_rsqf(__shfl(s, lane_of_sum(i)) + 1e-6f);
+      const float rk = __builtin_amdgcn_rsqf(__shfl(s, lane_of_sum(8 + i)) + 1e-6f);
       qn[i][0] *= rq; qn[i][1] *= rq;
       kn[i][0] *= rk; kn[i][1] *= rk;
     }
-    // Gate per key channel and its cumsum over this wave's rows (padding rows: g = 0).
+    // Gate per key channel and its cumsum over this wave's rows (padding rows: g = 0),
+    // in base 2.
+    const float lb2 = p.lower_bound * kLog2e;
     float run0 = 0.f, run1 = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const bool valid = 8 * w + i < len;
-      run0 += valid ? p.lower_bound * sigm(in.g[i].x) : 0.f;
-      run1 += valid ? p.lower_bound * sigm(in.g[i].y) : 0.f;
+      run0 += valid ? lb2 * sigm(in.g[i].x) : 0.f;
+      run1 += valid ? lb2 * sigm(in.g[i].y) : 0.f;
       G[i][0] = run0;
       G[i][1] = run1;
     }
@@ -260,21 +272,19 @@ __device__ void process_item(const Plan& p, const Item& it, const Inputs& in, ch
 
   // ---------------------------------------------------------------- A and P on MFMA
   {
-    __bf16 lkh[8][2], lkl[8][2], lqh[8][2], lql[8][2];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int r = 8 * w + i;
       const float2 gm = *reinterpret_cast<const float2*>(Gref + (r / REF) * 128 + c0);
-      const float e0 = __expf(G[i][0] - gm.x), e1 = __expf(G[i][1] - gm.y);  // in [e^-80, 1]
-      split_bf16(kn[i][0] * e0, lkh[i][0], lkl[i][0]);
-      split_bf16(kn[i][1] * e1, lkh[i][1], lkl[i][1]);
-      split_bf16(qn[i][0] * e0, lqh[i][0], lql[i][0]);
-      split_bf16(qn[i][1] * e1, lqh[i][1], lql[i][1]);
+      const float e0 = ex2(G[i][0] - gm.x), e1 = ex2(G[i][1] - gm.y);  // in [e^-80, 1]
+      uint32_t kh, kl, qh, ql;
+      split2(kn[i][0] * e0, kn[i][1] * e1, kh, kl);
+      split2(qn[i][0] * e0, qn[i][1] * e1, qh, ql);
       const int o = (r * LDA + c0) * 2;
-      *reinterpret_cast<uint32_t*>(X + xLKh + o) = pack2(lkh[i][0], lkh[i][1]);
-      *reinterpret_cast<uint32_t*>(X + xLKl + o) = pack2(lkl[i][0], lkl[i][1]);
-      *reinterpret_cast<uint32_t*>(X + xLQh + o) = pack2(lqh[i][0], lqh[i][1]);
-      *reinterpret_cast<uint32_t*>(X + xLQl + o) = pack2(lql[i][0], lql[i][1]);
+      *reinterpret_cast<uint32_t*>(X + xLKh + o) = kh;
+      *reinterpret_cast<uint32_t*>(X + xLKl + o) = kl;
+      *reinterpret_cast<uint32_t*>(X + xLQh + o) = qh;
+      *reinterpret_cast<uint32_t*>(X + xLQl + o) = ql;
     }
   }
   const int l16 = lane & 15, g4 = lane >> 4;
@@ -293,27 +303,24 @@ __device__ void process_item(const Plan& p, const Item& it, const Inputs& in, ch
     {
       const float2 g0 = *reinterpret_cast<const float2*>(Gref + c0);
       const float2 g16 = *reinterpret_cast<const float2*>(Gref + 128 + c0);
-      const float d0 = __expf(g16.x - g0.x), d1 = __expf(g16.y - g0.y);  // e^{G_16 - G_0} <= 1
+      const float d0 = ex2(g16.x - g0.x), d1 = ex2(g16.y - g0.y);  // e^{G_16 - G_0} <= 1
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int r = 8 * w + i;
         const float2 gm = (r < 16) ? g0 : g16;
-        const float r0 = __expf(gm.x - G[i][0]), r1 = __expf(gm.y - G[i][1]);  // own block, <= e^80
-        __bf16 h0, l0, h1, l1;
+        const float r0 = ex2(gm.x - G[i][0]), r1 = ex2(gm.y - G[i][1]);  // own block, <= e^80
+        uint32_t h, l;
         const int o = (r * LDA + c0) * 2;
         if (r < 16) {
-          split_bf16(kn[i][0] * r0, h0, l0);
-          split_bf16(kn[i][1] * r1, h1, l1);
-          *reinterpret_cast<uint32_t*>(X + xR0h + o) = pack2(h0, h1);
-          *reinterpret_cast<uint32_t*>(X + xR0l + o) = pack2(l0, l1);
-          split_bf16(kn[i][0] * (r0 * d0), h0, l0);  // e^{G_16 - G_r} <= 1
-          split_bf16(kn[i][1] * (r1 * d1), h1, l1);
+          split2(kn[i][0] * r0, kn[i][1] * r1, h, l);
+          *reinterpret_cast<uint32_t*>(X + xR0h + o) = h;
+          *reinterpret_cast<uint32_t*>(X + xR0l + o) = l;
+          split2(kn[i][0] * (r0 * d0), kn[i][1] * (r1 * d1), h, l);  // e^{G_16 - G_r} <= 1
         } else {
-          split_bf16(kn[i][0] * r0, h0, l0);
-          split_bf16(kn[i][1] * r1, h1, l1);
+          split2(kn[i][0] * r0, kn[i][1] * r1, h, l);
         }
-        *reinterpret_cast<uint32_t*>(X + xRh + o) = pack2(h0, h1);
-        *reinterpret_cast<uint32_t*>(X + xRl + o) = pack2(l0, l1);
+        *reinterpret_cast<uint32_t*>(X + xRh + o) = h;
+        *reinterpret_cast<uint32_t*>(X + xRl + o) = l;
       }
     }
     __syncthreads();
@@ -350,15 +357,14 @@ __device__ void process_item(const Plan& p, const Item& it, const Inputs& in, ch
         const int r = 8 * w + i;
         float x0 = 0.f, x1 = 0.f;
         if (r <= lim) {
-          x0 = kn[i][0] * __expf(gm.x - G[i][0]);  // <= e^80
-          x1 = kn[i][1] * __expf(gm.y - G[i][1]);
+          x0 = kn[i][0] * ex2(gm.x - G[i][0]);  // <= e^80
+          x1 = kn[i][1] * ex2(gm.y - G[i][1]);
         }
-        __bf16 h0, l0, h1, l1;
-        split_bf16(x0, h0, l0);
-        split_bf16(x1, h1, l1);
+        uint32_t h, l;
+        split2(x0, x1, h, l);
         const int o = (r * LDA + c0) * 2;
-        *reinterpret_cast<uint32_t*>(X + xRh + o) = pack2(h0, h1);
-        *reinterpret_cast<uint32_t*>(X + xRl + o) = pack2(l0, l1);
+        *reinterpret_cast<uint32_t*>(X + xRh + o) = h;
+        *reinterpret_cast<uint32_t*>(X + xRl + o) = l;
       }
     }
     __syncthreads();
@@ -411,21 +417,28 @@ __device__ void process_item(const Plan& p, const Item& it, const Inputs& in, ch
   // (the factor tiles are dead after the last barrier of the loop above)
   {
     const float2 gc = *reinterpret_cast<const float2*>(Gref + NB * 128 + c0);
-    __bf16 kg0h[8], kg0l[8], kg1h[8], kg1l[8], kt0[8], kt1[8], v0[8], v1[8];
+    // Transposed tiles take rows in pairs: word j of a channel holds rows 2j, 2j + 1.
+    uint32_t kg0h[4], kg0l[4], kg1h[4], kg1l[4], kt0[4], kt1[4], v0[4], v1[4];
+    float eg[8][2];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
+      eg[i][0] = ex2(G[i][0]);  // e^{G_r} <= 1
+      eg[i][1] = ex2(G[i][1]);
       const int r = 8 * w + i;
-      const float eg0 = __expf(G[i][0]), eg1 = __expf(G[i][1]);            // e^{G_r} <= 1
-      const float ec0 = __expf(gc.x - G[i][0]), ec1 = __expf(gc.y - G[i][1]);  // e^{G_C - G_r} <= 1
-      split_bf16(kn[i][0] * eg0, kg0h[i], kg0l[i]);
-      split_bf16(kn[i][1] * eg1, kg1h[i], kg1l[i]);
-      kt0[i] = to_bf16(kn[i][0] * ec0);
-      kt1[i] = to_bf16(kn[i][1] * ec1);
-      const bool valid = r < len;
-      v0[i] = valid ? __builtin_bit_cast(__bf16, (uint16_t)(in.v[i] & 0xffffu)) : to_bf16(0.f);
-      v1[i] = valid ? __builtin_bit_cast(__bf16, (uint16_t)(in.v[i] >> 16)) : to_bf16(0.f);
       *reinterpret_cast<uint32_t*>(X + xQs + (r * LDA + c0) * 2) =
-          pack2(to_bf16(p.scale * qn[i][0] * eg0), to_bf16(p.scale * qn[i][1] * eg1));
+          cvt_pk(p.scale * qn[i][0] * eg[i][0], p.scale * qn[i][1] * eg[i][1]);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int i = 2 * j;
+      split2(kn[i][0] * eg[i][0], kn[i + 1][0] * eg[i + 1][0], kg0h[j], kg0l[j]);
+      split2(kn[i][1] * eg[i][1], kn[i + 1][1] * eg[i + 1][1], kg1h[j], kg1l[j]);
+      // e^{G_C - G_r} <= 1
+      kt0[j] = cvt_pk(kn[i][0] * ex2(gc.x - G[i][0]), kn[i + 1][0] * ex2(gc.x - G[i + 1][0]));
+      kt1[j] = cvt_pk(kn[i][1] * ex2(gc.y - G[i][1]), kn[i + 1][1] * ex2(gc.y - G[i + 1][1]));
+      const uint32_t m0 = (8 * w + i < len) ? 0xffffu : 0u, m1 = (8 * w + i + 1 < len) ? 0xffff0000u : 0u;
+      v0[j] = ((in.v[i] & 0xffffu) | (in.v[i + 1] << 16)) & (m0 | m1);
+      v1[j] = ((in.v[i] >> 16) | (in.v[i + 1] & 0xffff0000u)) & (m0 | m1);
     }
     st_col8(X, xKGh, c0, w, kg0h);
     st_col8(X, xKGh, c0 + 1, w, kg1h);
@@ -435,7 +448,7 @@ __device__ void process_item(const Plan& p, const Item& it, const Inputs& in, ch
     st_col8(X, xKt, c0 + 1, w, kt1);
     st_col8(X, xVt, c0, w, v0);
     st_col8(X, xVt, c0 + 1, w, v1);
-    if (w == 3) *reinterpret_cast<float2*>(rec + kRecE + c0 * 4) = make_float2(__expf(gc.x), __expf(gc.y));
+    if (w == 3) *reinterpret_cast<float2*>(rec + kRecE + c0 * 4) = make_float2(ex2(gc.x), ex2(gc.y));
   }
   __syncthreads();
 
@@ -514,17 +527,17 @@ __device__ void process_item(const Plan& p, const Item& it, const Inputs& in, ch
   __syncthreads();
   // T diag(beta) as hi/lo bf16 (rows r, column r'), zero above the diagonal.
   {
-    __bf16* Th = reinterpret_cast<__bf16*>(X + xTh);
-    __bf16* Tl = reinterpret_cast<__bf16*>(X + xTl);
+    // Thread: columns j, j + 1 of row i, twice.
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const int e = tid + 256 * q4;
-      const int i = e >> 5, j = e & 31;
-      const float x = (j <= i) ? Ts[i * LDF + j] * betas[j] : 0.f;
-      __bf16 hi, lo;
-      split_bf16(x, hi, lo);
-      Th[i * LDT + j] = hi;
-      Tl[i * LDT + j] = lo;
+    for (int q2 = 0; q2 < 2; ++q2) {
+      const int e = tid + 256 * q2;
+      const int i = e >> 4, j = 2 * (e & 15);
+      const float x0 = (j <= i) ? Ts[i * LDF + j] * betas[j] : 0.f;
+      const float x1 = (j + 1 <= i) ? Ts[i * LDF + j + 1] * betas[j + 1] : 0.f;
+      uint32_t hi, lo;
+      split2(x0, x1, hi, lo);
+      *reinterpret_cast<uint32_t*>(X + xTh + (i * LDT + j) * 2) = hi;
+      *reinterpret_cast<uint32_t*>(X + xTl + (i * LDT + j) * 2) = lo;
     }
   }
   __syncthreads();
