@@ -97,27 +97,38 @@ __device__ __forceinline__ Item item_of(const Plan& p, int item) {
   return it;
 }
 
-// Loads never depend on a branch (rows past the sequence are clamped into the tensor and
-// masked later) so that the next item's loads can stay in flight during compute.
+// Buffer descriptor over rows t0 .. t0 + len - 1 of head h of a [T][H][128] tensor with
+// elem-byte elements: loads from rows past the sequence fall outside the range and return
+// zero, which is the padding the method needs for q, k and v. The loads never depend on a
+// branch, so the next item's loads stay in flight during compute.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* base, const Item& it, int H, int elem) {
+  const char* b = reinterpret_cast<const char*>(base) + ((size_t)it.t0 * H + it.h) * kHead * elem;
+  const int bytes = it.len > 0 ? (it.len - 1) * H * kHead * elem + kHead * elem : 0;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(b), (short)0, bytes, kBufWord3);
+}
+
+template <bool GF32>
 __device__ __forceinline__ void load_inputs(const Plan& p, const Item& it, int w, int lane, Inputs& in) {
   const int H = p.H;
-  const int last = p.T - 1;
-  // Row pointers are uniform (scalar); the lane's channel pair is a 32-bit offset.
+  const __amdgpu_buffer_rsrc_t rq = rows_rsrc(p.q, it, H, 2), rk = rows_rsrc(p.k, it, H, 2),
+                               rv = rows_rsrc(p.v, it, H, 2), rg = rows_rsrc(p.g_raw, it, H, GF32 ? 4 : 2);
+  const int row2 = H * kHead * 2;  // bytes per token row of a 2-byte tensor
+  // The whole offset goes in the vector operand: the range check covers only that part.
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int row = min(it.t0 + 8 * w + i, last);
-    const size_t e = ((size_t)row * H + it.h) * kHead;
-    in.q[i] = reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint16_t*>(p.q) + e)[lane];
-    in.k[i] = reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint16_t*>(p.k) + e)[lane];
-    in.v[i] = reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint16_t*>(p.v) + e)[lane];
-    if (p.g_dtype == kF32) {
-      in.g[i] = reinterpret_cast<const float2*>(reinterpret_cast<const float*>(p.g_raw) + e)[lane];
+    const int vo = (8 * w + i) * row2 + lane * 4;
+    in.q[i] = __builtin_amdgcn_raw_buffer_load_b32(rq, vo, 0, 0);
+    in.k[i] = __builtin_amdgcn_raw_buffer_load_b32(rk, vo, 0, 0);
+    in.v[i] = __builtin_amdgcn_raw_buffer_load_b32(rv, vo, 0, 0);
+    if constexpr (GF32) {
+      const auto g = __builtin_amdgcn_raw_buffer_load_b64(rg, 2 * vo, 0, 0);
+      in.g[i] = make_float2(__uint_as_float(g[0]), __uint_as_float(g[1]));
     } else {
-      const uint32_t b = reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint16_t*>(p.g_raw) + e)[lane];
-      in.g[i] = make_float2(__uint_as_float(b << 16), __uint_as_float(b & 0xffff0000u));
+      const uint32_t g = __builtin_amdgcn_raw_buffer_load_b32(rg, vo, 0, 0);
+      in.g[i] = make_float2(__uint_as_float(g << 16), __uint_as_float(g & 0xffff0000u));
     }
   }
-  const int brow = min(it.t0 + 8 * w + (lane & 7), last);
+  const int brow = min(it.t0 + 8 * w + (lane & 7), p.T - 1);
   const size_t bidx = (size_t)brow * H + it.h;
   in.braw = (p.beta_dtype == kF32) ? reinterpret_cast<const float*>(p.beta_raw)[bidx]
                                    : bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(p.beta_raw)[bidx]);
@@ -192,6 +203,10 @@ __device__ __forceinline__ float wave_sum16(const float* x, int lane) {
   return s;
 }
 
+__device__ __forceinline__ float bcast(float x, int src) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), src));
+}
+
 __device__ __forceinline__ int lane_of_sum(int v) {
   return ((v >> 3) & 1) * 32 + ((v >> 2) & 1) * 16 + ((v >> 1) & 1) * 8 + (v & 1) * 4;
 }
@@ -217,21 +232,22 @@ __device__ void process_item(const Plan& p, const Item& it, const Inputs& in, ch
   float qn[8][2], kn[8][2], G[8][2];
   {
     float sq[16];
+    // Rows past the sequence were loaded as zeros.
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const bool valid = 8 * w + i < len;
-      qn[i][0] = valid ? lo16(in.q[i]) : 0.f;
-      qn[i][1] = valid ? hi16(in.q[i]) : 0.f;
-      kn[i][0] = valid ? lo16(in.k[i]) : 0.f;
-      kn[i][1] = valid ? hi16(in.k[i]) : 0.f;
+      qn[i][0] = lo16(in.q[i]);
+      qn[i][1] = hi16(in.q[i]);
+      kn[i][0] = lo16(in.k[i]);
+      kn[i][1] = hi16(in.k[i]);
       sq[i] = qn[i][0] * qn[i][0] + qn[i][1] * qn[i][1];
       sq[8 + i] = kn[i][0] * kn[i][0] + kn[i][1] * kn[i][1];
     }
-    const float s = wave_sum16(sq, lane);
+    // Each lane takes the inverse norm of the row sum it holds; rows read theirs back.
+    const float rs = __builtin_amdgcn_rsqf(wave_sum16(sq, lane) + 1e-6f);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float rq = __builtin_amdgcn_rsqf(__shfl(s, lane_of_sum(i)) + 1e-6f);
-      const float rk = __builtin_amdgcn_rsqf(__shfl(s, lane_of_sum(8 + i)) + 1e-6f);
+      const float rq = bcast(rs, lane_of_sum(i));
+      const float rk = bcast(rs, lane_of_sum(8 + i));
       qn[i][0] *= rq; qn[i][1] *= rq;
       kn[i][0] *= rk; kn[i][1] *= rk;
     }
@@ -271,11 +287,23 @@ __device__ void process_item(const Plan& p, const Item& it, const Inputs& in, ch
   __syncthreads();
 
   // ---------------------------------------------------------------- A and P on MFMA
+  // At REF = 16 the record's Q, K and KG tiles are formed here from the decay factors
+  // (e^{G_r} = e^{G_r - G_m} e^{G_m}, e^{G_C - G_r} = e^{G_C - G_16} e^{G_16 - G_r}, every
+  // factor inside the fp32 range) and kept packed until staging.
+  [[maybe_unused]] uint32_t qs[8], kg0h[4], kg0l[4], kg1h[4], kg1l[4], kt0[4], kt1[4];
   {
+    [[maybe_unused]] float kgv[8][2];
+    // The wave's 8 rows share one reference row when REF >= 8.
+    const float2 gw = *reinterpret_cast<const float2*>(Gref + (REF >= 8 ? (8 * w / REF) : 0) * 128 + c0);
+    [[maybe_unused]] float em0 = 0.f, em1 = 0.f;
+    if constexpr (REF == 16) {
+      em0 = ex2(gw.x);  // e^{G_m}, m = 0 or 16: inside the fp32 range at REF = 16
+      em1 = ex2(gw.y);
+    }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int r = 8 * w + i;
-      const float2 gm = *reinterpret_cast<const float2*>(Gref + (r / REF) * 128 + c0);
+      const float2 gm = REF >= 8 ? gw : *reinterpret_cast<const float2*>(Gref + (r / REF) * 128 + c0);
       const float e0 = ex2(G[i][0] - gm.x), e1 = ex2(G[i][1] - gm.y);  // in [e^-80, 1]
       uint32_t kh, kl, qh, ql;
       split2(kn[i][0] * e0, kn[i][1] * e1, kh, kl);
@@ -285,6 +313,19 @@ __device__ void process_item(const Plan& p, const Item& it, const Inputs& in, ch
       *reinterpret_cast<uint32_t*>(X + xLKl + o) = kl;
       *reinterpret_cast<uint32_t*>(X + xLQh + o) = qh;
       *reinterpret_cast<uint32_t*>(X + xLQl + o) = ql;
+      if constexpr (REF == 16) {
+        const float eg0 = e0 * em0, eg1 = e1 * em1;  // e^{G_r}
+        qs[i] = cvt_pk(p.scale * qn[i][0] * eg0, p.scale * qn[i][1] * eg1);
+        kgv[i][0] = kn[i][0] * eg0;
+        kgv[i][1] = kn[i][1] * eg1;
+      }
+    }
+    if constexpr (REF == 16) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        split2(kgv[2 * j][0], kgv[2 * j + 1][0], kg0h[j], kg0l[j]);
+        split2(kgv[2 * j][1], kgv[2 * j + 1][1], kg1h[j], kg1l[j]);
+      }
     }
   }
   const int l16 = lane & 15, g4 = lane >> 4;
@@ -303,7 +344,10 @@ __device__ void process_item(const Plan& p, const Item& it, const Inputs& in, ch
     {
       const float2 g0 = *reinterpret_cast<const float2*>(Gref + c0);
       const float2 g16 = *reinterpret_cast<const float2*>(Gref + 128 + c0);
+      const float2 gc = *reinterpret_cast<const float2*>(Gref + NB * 128 + c0);
       const float d0 = ex2(g16.x - g0.x), d1 = ex2(g16.y - g0.y);  // e^{G_16 - G_0} <= 1
+      const float c0e = ex2(gc.x - g16.x), c1e = ex2(gc.y - g16.y);  // e^{G_C - G_16} >= e^-80
+      float ktv[8][2];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int r = 8 * w + i;
@@ -311,16 +355,24 @@ __device__ void process_item(const Plan& p, const Item& it, const Inputs& in, ch
         const float r0 = ex2(gm.x - G[i][0]), r1 = ex2(gm.y - G[i][1]);  // own block, <= e^80
         uint32_t h, l;
         const int o = (r * LDA + c0) * 2;
+        float b0 = r0, b1 = r1;  // e^{G_16 - G_r}
         if (r < 16) {
           split2(kn[i][0] * r0, kn[i][1] * r1, h, l);
           *reinterpret_cast<uint32_t*>(X + xR0h + o) = h;
           *reinterpret_cast<uint32_t*>(X + xR0l + o) = l;
-          split2(kn[i][0] * (r0 * d0), kn[i][1] * (r1 * d1), h, l);  // e^{G_16 - G_r} <= 1
-        } else {
-          split2(kn[i][0] * r0, kn[i][1] * r1, h, l);
+          b0 = r0 * d0;  // <= 1
+          b1 = r1 * d1;
         }
+        split2(kn[i][0] * b0, kn[i][1] * b1, h, l);
         *reinterpret_cast<uint32_t*>(X + xRh + o) = h;
         *reinterpret_cast<uint32_t*>(X + xRl + o) = l;
+        ktv[i][0] = kn[i][0] * (b0 * c0e);  // k e^{G_C - G_r}
+        ktv[i][1] = kn[i][1] * (b1 * c1e);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        kt0[j] = cvt_pk(ktv[2 * j][0], ktv[2 * j + 1][0]);
+        kt1[j] = cvt_pk(ktv[2 * j][1], ktv[2 * j + 1][1]);
       }
     }
     __syncthreads();
@@ -399,11 +451,13 @@ __device__ void process_item(const Plan& p, const Item& it, const Inputs& in, ch
     for (int jb = 0; jb < 2; ++jb) {
       if (jb >= njobs) break;
       const int mat = (w < 2) ? jb : (w - 2);
+      float* dst = mat ? Ps : As;
+      const int diag = mat;  // P keeps its diagonal, A does not
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = 16 * jt + 4 * g4 + i;
-        if (mat == 0) As[row * LDF + col] = (col < row) ? betas[row] * acc[jb][i] : 0.f;
-        else Ps[row * LDF + col] = (col <= row) ? p.scale * acc[jb][i] : 0.f;
+        const float sc = mat ? p.scale : betas[row];
+        dst[row * LDF + col] = (col < row + diag) ? sc * acc[jb][i] : 0.f;
       }
     }
     if (w >= 2) {  // upper tile (0,1) of A (wave 2) and of P (wave 3)
@@ -418,27 +472,32 @@ __device__ void process_item(const Plan& p, const Item& it, const Inputs& in, ch
   {
     const float2 gc = *reinterpret_cast<const float2*>(Gref + NB * 128 + c0);
     // Transposed tiles take rows in pairs: word j of a channel holds rows 2j, 2j + 1.
-    uint32_t kg0h[4], kg0l[4], kg1h[4], kg1l[4], kt0[4], kt1[4], v0[4], v1[4];
-    float eg[8][2];
+    uint32_t v0[4], v1[4];
+    if constexpr (REF != 16) {
+      float eg[8][2];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      eg[i][0] = ex2(G[i][0]);  // e^{G_r} <= 1
-      eg[i][1] = ex2(G[i][1]);
-      const int r = 8 * w + i;
-      *reinterpret_cast<uint32_t*>(X + xQs + (r * LDA + c0) * 2) =
-          cvt_pk(p.scale * qn[i][0] * eg[i][0], p.scale * qn[i][1] * eg[i][1]);
+      for (int i = 0; i < 8; ++i) {
+        eg[i][0] = ex2(G[i][0]);  // e^{G_r} <= 1
+        eg[i][1] = ex2(G[i][1]);
+        qs[i] = cvt_pk(p.scale * qn[i][0] * eg[i][0], p.scale * qn[i][1] * eg[i][1]);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int i = 2 * j;
+        split2(kn[i][0] * eg[i][0], kn[i + 1][0] * eg[i + 1][0], kg0h[j], kg0l[j]);
+        split2(kn[i][1] * eg[i][1], kn[i + 1][1] * eg[i + 1][1], kg1h[j], kg1l[j]);
+        // e^{G_C - G_r} <= 1
+        kt0[j] = cvt_pk(kn[i][0] * ex2(gc.x - G[i][0]), kn[i + 1][0] * ex2(gc.x - G[i + 1][0]));
+        kt1[j] = cvt_pk(kn[i][1] * ex2(gc.y - G[i][1]), kn[i + 1][1] * ex2(gc.y - G[i + 1][1]));
+      }
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int i = 0; i < 8; ++i) *reinterpret_cast<uint32_t*>(X + xQs + ((8 * w + i) * LDA + c0) * 2) = qs[i];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {  // padding rows of v were loaded as zeros
       const int i = 2 * j;
-      split2(kn[i][0] * eg[i][0], kn[i + 1][0] * eg[i + 1][0], kg0h[j], kg0l[j]);
-      split2(kn[i][1] * eg[i][1], kn[i + 1][1] * eg[i + 1][1], kg1h[j], kg1l[j]);
-      // e^{G_C - G_r} <= 1
-      kt0[j] = cvt_pk(kn[i][0] * ex2(gc.x - G[i][0]), kn[i + 1][0] * ex2(gc.x - G[i + 1][0]));
-      kt1[j] = cvt_pk(kn[i][1] * ex2(gc.y - G[i][1]), kn[i + 1][1] * ex2(gc.y - G[i + 1][1]));
-      const uint32_t m0 = (8 * w + i < len) ? 0xffffu : 0u, m1 = (8 * w + i + 1 < len) ? 0xffff0000u : 0u;
-      v0[j] = ((in.v[i] & 0xffffu) | (in.v[i + 1] << 16)) & (m0 | m1);
-      v1[j] = ((in.v[i] >> 16) | (in.v[i + 1] & 0xffff0000u)) & (m0 | m1);
+      v0[j] = (in.v[i] & 0xffffu) | (in.v[i + 1] << 16);
+      v1[j] = (in.v[i] >> 16) | (in.v[i + 1] & 0xffff0000u);
     }
     st_col8(X, xKGh, c0, w, kg0h);
     st_col8(X, xKGh, c0 + 1, w, kg1h);
@@ -580,7 +639,7 @@ __device__ void process_item(const Plan& p, const Item& it, const Inputs& in, ch
   }
 }
 
-template <int REF>
+template <int REF, bool GF32>
 __global__ __launch_bounds__(kThreadsPrep, 2) void prep_kernel(Plan p, int n_items) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -592,34 +651,45 @@ __global__ __launch_bounds__(kThreadsPrep, 2) void prep_kernel(Plan p, int n_ite
   // before each item covers only its own inputs.
   Inputs ia, ib;
   Item ta = item_of(p, item), tb;
-  load_inputs(p, ta, w, lane, ia);
+  load_inputs<GF32>(p, ta, w, lane, ia);
   for (;;) {
     tb = item_of(p, min(item + step, n_items - 1));
-    load_inputs(p, tb, w, lane, ib);
+    load_inputs<GF32>(p, tb, w, lane, ib);
     process_item<REF>(p, ta, ia, lds, w, lane);
     item += step;
     if (item >= n_items) break;
     ta = item_of(p, min(item + step, n_items - 1));
-    load_inputs(p, ta, w, lane, ia);
+    load_inputs<GF32>(p, ta, w, lane, ia);
     process_item<REF>(p, tb, ib, lds, w, lane);
     item += step;
     if (item >= n_items) break;
   }
 }
 
-template <int REF>
+template <int REF, bool GF32>
 int launch_ref(const Plan& p, hipStream_t s, int grid, hipEvent_t start, hipEvent_t stop) {
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prep_kernel<REF>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prep_kernel<REF, GF32>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes(REF));
     if (e != hipSuccess) return (int)e;
     attr_set = true;
   }
   const int n_items = p.n_chunks * p.H;
-  hipExtLaunchKernelGGL(prep_kernel<REF>, dim3(min(grid, n_items)), dim3(kThreadsPrep), lds_bytes(REF), s, start, stop,
-                        0, p, n_items);
+  hipExtLaunchKernelGGL((prep_kernel<REF, GF32>), dim3(min(grid, n_items)), dim3(kThreadsPrep), lds_bytes(REF), s,
+                        start, stop, 0, p, n_items);
   return (int)hipGetLastError();
+}
+
+template <bool GF32>
+int launch_gate(const Plan& p, hipStream_t s, int grid, hipEvent_t e0, hipEvent_t e1) {
+  switch (p.ref_block) {
+    case 16: return launch_ref<16, GF32>(p, s, grid, e0, e1);
+    case 8: return launch_ref<8, GF32>(p, s, grid, e0, e1);
+    case 4: return launch_ref<4, GF32>(p, s, grid, e0, e1);
+    case 2: return launch_ref<2, GF32>(p, s, grid, e0, e1);
+    default: return launch_ref<1, GF32>(p, s, grid, e0, e1);
+  }
 }
 
 }  // namespace
@@ -629,13 +699,7 @@ int launch_prep(const Plan& p, void* stream, void* start, void* stop) {
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipEvent_t e0 = reinterpret_cast<hipEvent_t>(start), e1 = reinterpret_cast<hipEvent_t>(stop);
   const int grid = 2 * p.cu_count;  // persistent: two resident workgroups per CU
-  switch (p.ref_block) {
-    case 16: return launch_ref<16>(p, s, grid, e0, e1);
-    case 8: return launch_ref<8>(p, s, grid, e0, e1);
-    case 4: return launch_ref<4>(p, s, grid, e0, e1);
-    case 2: return launch_ref<2>(p, s, grid, e0, e1);
-    default: return launch_ref<1>(p, s, grid, e0, e1);
-  }
+  return p.g_dtype == kF32 ? launch_gate<true>(p, s, grid, e0, e1) : launch_gate<false>(p, s, grid, e0, e1);
 }
 
 }  // namespace kda
