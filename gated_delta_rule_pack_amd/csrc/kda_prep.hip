@@ -90,10 +90,11 @@ __device__ __forceinline__ Item item_of(const Plan& p, int item) {
   Item it;
   it.cid = item / p.H;
   it.h = item - it.cid * p.H;
-  it.seq = p.d_table[2 * it.cid];
-  const int jc = p.d_table[2 * it.cid + 1];
-  it.t0 = p.d_cu[it.seq] + kChunk * jc;
-  it.len = min(kChunk, p.d_cu[it.seq + 1] - it.t0);
+  // Uniform metadata, kept in scalar registers (see the scan's unit lookup).
+  it.seq = __builtin_amdgcn_readfirstlane(p.d_table[2 * it.cid]);
+  const int jc = __builtin_amdgcn_readfirstlane(p.d_table[2 * it.cid + 1]);
+  it.t0 = __builtin_amdgcn_readfirstlane(p.d_cu[it.seq]) + kChunk * jc;
+  it.len = min(kChunk, __builtin_amdgcn_readfirstlane(p.d_cu[it.seq + 1]) - it.t0);
   return it;
 }
 
@@ -128,10 +129,16 @@ __device__ __forceinline__ void load_inputs(const Plan& p, const Item& it, int w
       in.g[i] = make_float2(__uint_as_float(g << 16), __uint_as_float(g & 0xffff0000u));
     }
   }
+  // Raw beta of row 8w + (lane & 7) as two 2-byte loads (the upper and lower halves of
+  // an fp32 value, or the bf16 value twice), so no branch holds the loads back and no
+  // byte outside the element is read.
   const int brow = min(it.t0 + 8 * w + (lane & 7), p.T - 1);
   const size_t bidx = (size_t)brow * H + it.h;
-  in.braw = (p.beta_dtype == kF32) ? reinterpret_cast<const float*>(p.beta_raw)[bidx]
-                                   : bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(p.beta_raw)[bidx]);
+  const bool bf = p.beta_dtype != kF32;
+  const char* bb = reinterpret_cast<const char*>(p.beta_raw);
+  const uint32_t bhi = *reinterpret_cast<const uint16_t*>(bb + (bf ? bidx * 2 : bidx * 4 + 2));
+  const uint32_t blo = *reinterpret_cast<const uint16_t*>(bb + (bf ? bidx * 2 : bidx * 4));
+  in.braw = __uint_as_float((bhi << 16) | (bf ? 0u : blo));
 }
 
 __device__ __forceinline__ float lo16(uint32_t x) { return __uint_as_float(x << 16); }

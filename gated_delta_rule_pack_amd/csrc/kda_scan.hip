@@ -75,22 +75,26 @@ struct Unit {
 // halves A and C.
 template <int KMODE>
 __device__ __forceinline__ bool unit_of(const Plan& p, int units, int groups, Unit& u) {
+  // Every field is uniform. readfirstlane keeps each in a scalar register: the integer
+  // divisions below run on vector ALUs, and the compiler cannot always prove the loads
+  // unclobbered; a buffer descriptor built from vector registers would make every load
+  // that uses it loop over the lanes.
   const int bidx = blockIdx.x;
   const int xcd = bidx & 7;
   const int slot8 = bidx >> 3;
-  const int local = slot8 / groups;
-  u.grp = slot8 - local * groups;
+  const int local = __builtin_amdgcn_readfirstlane(slot8 / groups);
+  u.grp = __builtin_amdgcn_readfirstlane(slot8 - local * groups);
   const int id = local * 8 + xcd;
   if (id >= units) return false;
-  const int q = id / p.H;
-  u.h = id - q * p.H;
-  const int s = KMODE == kKernelScan ? q : p.d_m2s[q];
+  const int q = __builtin_amdgcn_readfirstlane(id / p.H);
+  u.h = __builtin_amdgcn_readfirstlane(id - q * p.H);
+  const int s = KMODE == kKernelScan ? q : __builtin_amdgcn_readfirstlane(p.d_m2s[q]);
   const int32_t* e = p.d_seg + (size_t)kSegInts * s;
-  u.n = e[0];
-  u.c0 = e[1];
-  u.nch = e[2];
-  u.m_prev = e[3];
-  u.m_self = KMODE == kKernelScan ? e[4] : q;
+  u.n = __builtin_amdgcn_readfirstlane(e[0]);
+  u.c0 = __builtin_amdgcn_readfirstlane(e[1]);
+  u.nch = __builtin_amdgcn_readfirstlane(e[2]);
+  u.m_prev = __builtin_amdgcn_readfirstlane(e[3]);
+  u.m_self = KMODE == kKernelScan ? __builtin_amdgcn_readfirstlane(e[4]) : q;
   return true;
 }
 
@@ -164,9 +168,10 @@ __global__ __launch_bounds__(320, 1) void head_kernel(Plan p, int units, int gro
   const int lane = threadIdx.x & 63, g4 = lane >> 4, l16 = lane & 15;
   const int vo = lane * 16;  // lane offset inside a fragment
   const int nc = un.nch;
-  const int cu0 = p.d_cu[n] + kChunk * un.c0, cu1 = p.d_cu[n + 1];  // segment start, sequence end
-  const char* rec0 =
-      reinterpret_cast<const char*>(p.ws) + ((size_t)h * p.n_chunks + p.d_co[n] + un.c0) * kRecBytes;
+  const int cu0 = __builtin_amdgcn_readfirstlane(p.d_cu[n]) + kChunk * un.c0;  // segment start
+  const int cu1 = __builtin_amdgcn_readfirstlane(p.d_cu[n + 1]);              // sequence end
+  const int co = __builtin_amdgcn_readfirstlane(p.d_co[n]);
+  const char* rec0 = reinterpret_cast<const char*>(p.ws) + ((size_t)h * p.n_chunks + co + un.c0) * kRecBytes;
   const __amdgpu_buffer_rsrc_t rs =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(rec0), (short)0, nc * (int)kRecBytes, kBufWord3);
   // Value tiles of the workgroup start at u0 (scan: its half; map: all 8).
@@ -436,10 +441,11 @@ __global__ __launch_bounds__(256, 1) void scan_narrow(Plan p, int units, int gro
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, g4 = lane >> 4, l16 = lane & 15;
   const int vtile0 = un.grp * NT;  // first 16-channel value tile of this workgroup
-  const int cu0 = p.d_cu[n] + kChunk * un.c0, cu1 = p.d_cu[n + 1];  // segment start, sequence end
+  const int cu0 = __builtin_amdgcn_readfirstlane(p.d_cu[n]) + kChunk * un.c0;  // segment start
+  const int cu1 = __builtin_amdgcn_readfirstlane(p.d_cu[n + 1]);              // sequence end
   const int nc = un.nch;
-  const char* rec0 =
-      reinterpret_cast<const char*>(p.ws) + ((size_t)h * p.n_chunks + p.d_co[n] + un.c0) * kRecBytes;
+  const int co = __builtin_amdgcn_readfirstlane(p.d_co[n]);
+  const char* rec0 = reinterpret_cast<const char*>(p.ws) + ((size_t)h * p.n_chunks + co + un.c0) * kRecBytes;
   const __amdgpu_buffer_rsrc_t rs =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(rec0), (short)0, nc * (int)kRecBytes, kBufWord3);
   const int vo = lane * 16;  // lane offset inside a fragment
@@ -456,13 +462,17 @@ __global__ __launch_bounds__(256, 1) void scan_narrow(Plan p, int units, int gro
       char* base = lds + slot * L::kSlot;
       const int soff = c * (int)kRecBytes;
 #pragma unroll
-      for (int f = 0; f < 8; ++f)
+      for (int g = 0; g < 8; ++g) {  // the workgroups of a head start at different fragments
+        const int f = (g + un.grp) & 7;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(base + L::kSlotW + f * 1024), 16, vo,
                                                  soff + (int)kRecW + f * (int)kFrag, 0, 0);
+      }
 #pragma unroll
-      for (int f = 0; f < 8; ++f)
+      for (int g = 0; g < 8; ++g) {
+        const int f = (g + un.grp) & 7;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(base + L::kSlotK + f * 1024), 16, vo,
                                                  soff + (int)kRecK + f * (int)kFrag, 0, 0);
+      }
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(base + L::kSlotU + nt * 1024), 16, vo,
