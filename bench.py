@@ -89,12 +89,29 @@ def cpu_baseline(wl, max_tokens: int, workers: int, min_seconds: float):
                 wall = time.perf_counter() - t0
                 if wall >= min_seconds:
                     break
+        # One core: one head in this process, repeated for a quarter of the time; the
+        # rate scales by the number of heads.
+        reps1 = 0
+        t1 = time.perf_counter()
+        while True:
+            _oracle_head(tasks[0])
+            reps1 += 1
+            wall1 = time.perf_counter() - t1
+            if wall1 >= min_seconds / 4:
+                break
     tokens = int(cu_s[-1])
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "")
+    except OSError:
+        pass
     return {
         "value": reps * tokens / wall, "unit": "tokens/s", "cores": workers, "kind": "oracle",
         "sample": f"first {tokens} tokens ({take} sequence(s)) of the workload, all {wl.H} heads, "
                   f"one head per worker process, fp64 numpy token loop, {reps} pass(es)",
         "seconds": wall,
+        "value_1core": reps1 * tokens / (wall1 * wl.H), "cpu_model": model, "nproc": os.cpu_count(),
     }
 
 
@@ -180,6 +197,9 @@ def main():
     ap.add_argument("--workload", choices=sorted(WORKLOADS), default="paged_1x4096_H12")
     ap.add_argument("--rotate", type=int, default=0,
                     help="input sets cycled through (0: enough to exceed the 256 MB MALL)")
+    ap.add_argument("--rotate-bounds", type=int, default=0,
+                    help="cycle through this many permutations of the sequence lengths (metadata-cache "
+                         "miss mode: every call uploads its metadata)")
     ap.add_argument("--cpu-tokens", type=int, default=4096, help="oracle sample size (tokens)")
     ap.add_argument("--cpu-workers", type=int, default=12)
     ap.add_argument("--cpu-seconds", type=float, default=2.0, help="minimum oracle wall time")
@@ -233,16 +253,33 @@ def main():
         state = dict(state_cache=storage.as_strided((wl.num_slots, wl.H, 128, 128),
                                                     (wl.state_stride0, 128 * 128, 128, 1)),
                      state_indices=wl.state_indices.to(dev), has_initial_state=wl.has_initial_state.to(dev))
-    sets = []
+    # Bounds sets: the workload's own, or (--rotate-bounds K) K seeded permutations of its
+    # sequence lengths, so that every call misses the metadata cache (64 entries).
+    bounds = [(cu_d, cu_h)]
+    if args.rotate_bounds:
+        gen = torch.Generator().manual_seed(7)
+        lens = wl.cu_seqlens[1:] - wl.cu_seqlens[:-1]
+        bounds = []
+        for _ in range(args.rotate_bounds):
+            perm = lens[torch.randperm(wl.N, generator=gen)]
+            h_cu = torch.cat([torch.zeros(1, dtype=torch.int32), torch.cumsum(perm, 0).to(torch.int32)])
+            bounds.append((h_cu.to(dev), h_cu))
+    inputs = []
     for i in range(n_rot):
         s = {n: (t if i == 0 else t.clone()) for n, t in base.items()}
         s["out"] = torch.empty_like(s["v"])
-        a = kda.make_args(s["q"], s["k"], s["v"], s["g_raw"], s["beta_raw"], cu_d, cu_seqlens_cpu=cu_h,
+        inputs.append(s)
+    sets = []  # (inputs, args, bounds tensors kept alive)
+    for i in range(max(n_rot, len(bounds))):
+        s = inputs[i % n_rot]
+        b_d, b_h = bounds[i % len(bounds)]
+        a = kda.make_args(s["q"], s["k"], s["v"], s["g_raw"], s["beta_raw"], b_d, cu_seqlens_cpu=b_h,
                           scale=wl.scale, lower_bound=wl.lower_bound, out=s["out"], **state)
         rc = lib.kda_chunk_fwd_validate(ctypes.byref(a))
         if rc != _lib.KDA_OK:
             raise kda.KDAError(rc, "validate")
-        sets.append((s, a))
+        sets.append((s, a, (b_d, b_h)))
+    n_rot = len(sets)
     ws_bytes = kda.workspace_bytes(sets[0][1])
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     ws_p, ws_n, st_p = ctypes.c_void_p(ws.data_ptr()), ctypes.c_size_t(ws_bytes), ctypes.c_void_p(stream.cuda_stream)
@@ -275,7 +312,9 @@ def main():
         step(i)
     torch.cuda.synchronize()
     ctx.profile(False)
+    per_call = sorted(ctx.profile_calls(args.steps))
     prep_ms, scan_ms, ncalls = ctx.profile_read()
+    pct = lambda f: 1e3 * per_call[min(len(per_call) - 1, int(f * len(per_call)))]
     ms_total = e0.elapsed_time(e1)
     ms_step = ms_total / args.steps
     tokens = wl.T
@@ -303,8 +342,12 @@ def main():
         "config": {"workload": args.workload, "description": cfg_desc, "T": wl.T, "N": wl.N, "H": wl.H, "K": 128, "V": 128, "chunk": 32,
                    "lower_bound": wl.lower_bound, "state": f"{wl.state_mode} {wl.state_dtype}",
                    "dv_split": stats["last_dv_split"], "ref_block": stats["last_ref_block"],
-                   "input_sets_rotated": n_rot, "parallelism": "single GPU"},
+                   "input_sets_rotated": n_rot, "bounds_sets": max(1, args.rotate_bounds),
+                   "parallelism": "single GPU"},
         "kernels_us": {k: round(v, 2) for k, v in k_us.items()},
+        # Per-call latency from the kernels' own timestamps (first kernel start to scan
+        # end), over the profiled pass.
+        "call_us_p10_p50_p90": [round(pct(0.1), 2), round(pct(0.5), 2), round(pct(0.9), 2)],
         "host_wall_us_per_call": round(wall / args.steps * 1e6, 2),
         "metadata": {"cache_hits": stats["cache_hits"], "cache_misses": stats["cache_misses"],
                      "blocking_syncs": stats["blocking_syncs"]},

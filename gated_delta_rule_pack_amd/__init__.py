@@ -47,6 +47,15 @@ class Context:
         """Record per-kernel timing events in every following call (or stop)."""
         _lib.load().kda_profile_enable(self.ptr, 1 if enable else 0)
 
+    def profile_calls(self, cap: int = 4096):
+        """Per-call durations (ms, first kernel start to scan end) of the recorded calls."""
+        buf = (ctypes.c_float * cap)()
+        n = ctypes.c_int64()
+        rc = _lib.load().kda_profile_calls(self.ptr, buf, cap, ctypes.byref(n))
+        if rc != _lib.KDA_OK:
+            raise KDAError(rc, "kda_profile_calls")
+        return [buf[i] for i in range(min(n.value, cap))]
+
     def profile_read(self):
         """(prep_ms_total, scan_ms_total, calls) since the last read; waits for the events."""
         a, b, n = ctypes.c_double(), ctypes.c_double(), ctypes.c_int64()

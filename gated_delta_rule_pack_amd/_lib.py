@@ -135,6 +135,8 @@ def load() -> ctypes.CDLL:
     lib.kda_profile_enable.argtypes = [P, c_int]
     lib.kda_profile_read.restype = c_int
     lib.kda_profile_read.argtypes = [P, POINTER(ctypes.c_double), POINTER(ctypes.c_double), POINTER(c_int64)]
+    lib.kda_profile_calls.restype = c_int
+    lib.kda_profile_calls.argtypes = [P, POINTER(c_float), c_int64, POINTER(c_int64)]
     lib.kda_fwd_args_size.restype = c_size_t
     lib.kda_fwd_args_size.argtypes = []
     if lib.kda_fwd_args_size() != ctypes.sizeof(FwdArgs):
@@ -153,4 +155,5 @@ EXPORTS = [
     "kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd_validate", "kda_chunk_fwd",
     "kda_prepare_chunk_indices", "kda_dv_split", "kda_seg_len", "kda_ref_block", "kda_fwd_args_size",
     "kda_status_str", "kda_get_stats", "kda_reset_stats", "kda_profile_enable", "kda_profile_read",
+    "kda_profile_calls",
 ]

@@ -766,6 +766,23 @@ kda_status kda_profile_read(kda_ctx* ctx, double* prep_ms, double* scan_ms, int6
   return KDA_OK;
 }
 
+kda_status kda_profile_calls(kda_ctx* ctx, float* call_ms, int64_t cap, int64_t* n) {
+  if (!ctx || !n || (cap > 0 && !call_ms)) return KDA_ERR_INVALID_ARG;
+  auto& rt = ctx->rt;
+  int64_t i = 0;
+  for (auto& m : ctx->marks) {
+    if (i < cap) {
+      if (rt.event_synchronize(rt.user, m.ev[3])) return hip_fail();
+      float x = 0.f;
+      if (rt.event_elapsed_ms(rt.user, &x, m.prep ? m.ev[0] : m.ev[2], m.ev[3])) return hip_fail();
+      call_ms[i] = x;
+    }
+    ++i;
+  }
+  *n = i;
+  return KDA_OK;
+}
+
 size_t kda_fwd_args_size(void) { return sizeof(kda_fwd_args); }
 
 }  // extern "C"

@@ -212,12 +212,19 @@ int32_t kda_seg_len(int32_t n_seqs, int32_t H, int64_t max_chunks);
  * Optimizations Applied: bounded construction, NaN-free to 640 nats). */
 int32_t kda_ref_block(float lower_bound);
 
-/* Per-kernel timing, off by default. While enabled, each kda_chunk_fwd records timing
- * events on its stream before prep, between prep and scan, and after scan.
- * kda_profile_read waits for the recorded events, adds up the prep and scan durations
- * in milliseconds, reports how many calls they cover, and clears them. */
+/* Per-kernel timing, off by default. While enabled, each kda_chunk_fwd attaches timing
+ * events to its kernel launches (start and end of prep; start of the first scan-phase
+ * kernel and end of the scan), so the durations are the kernels' own, with no marker in
+ * the stream. kda_profile_read waits for the recorded events, adds up the prep and scan
+ * durations in milliseconds, reports how many calls they cover, and clears them.
+ * kda_profile_calls (call it before kda_profile_read) writes, in call order, up to cap
+ * per-call durations in milliseconds, from the start of the call's first kernel to the
+ * end of its scan, sets *n to the number of recorded calls and clears nothing.
+ * Both return KDA_ERR_INVALID_ARG for null pointers (call_ms may be null when cap is 0)
+ * and KDA_ERR_HIP if an event query fails. */
 kda_status kda_profile_enable(kda_ctx* ctx, int enable);
 kda_status kda_profile_read(kda_ctx* ctx, double* prep_ms, double* scan_ms, int64_t* calls);
+kda_status kda_profile_calls(kda_ctx* ctx, float* call_ms, int64_t cap, int64_t* n);
 
 /* sizeof(kda_fwd_args), so a binding can check its mirror of the struct. */
 size_t kda_fwd_args_size(void);

@@ -415,6 +415,11 @@ def test_profiling_attaches_timing_events_to_launches(lib, fake):
     fake.launches.clear()
     assert _call(lib, fake, b) == _lib.KDA_OK
     assert fake.launches == [(1, 0x10)]
+    per_call, n = (ctypes.c_float * 4)(), ctypes.c_int64()
+    assert lib.kda_profile_calls(fake.ctx, per_call, 4, ctypes.byref(n)) == _lib.KDA_OK
+    assert n.value == 2 and list(per_call)[:2] == [1.0, 1.0]  # first kernel start to scan end
+    assert lib.kda_profile_calls(fake.ctx, None, 0, ctypes.byref(n)) == _lib.KDA_OK and n.value == 2
+    assert lib.kda_profile_calls(fake.ctx, None, 4, ctypes.byref(n)) == _lib.KDA_ERR_INVALID_ARG
     prep, scan, calls = ctypes.c_double(), ctypes.c_double(), ctypes.c_int64()
     assert lib.kda_profile_read(fake.ctx, ctypes.byref(prep), ctypes.byref(scan), ctypes.byref(calls)) == _lib.KDA_OK
     assert calls.value == 2 and prep.value == 1.0 and scan.value == 2.0
