@@ -1,0 +1,240 @@
+// Decode kernel: the recurrent step for calls in which every sequence has at most one
+// token. Decode goes through a fused update kernel rather than the chunked path (aiter
+// PR 4741, Performance), and it is bound by state bandwidth, with the state read and
+// written at its storage dtype and accumulated in fp32 (aiter PR 5249, Why).
+//
+// Per (sequence, head), with the token's q-hat, k-hat, v, g = lb * sigmoid(g_raw) and
+// beta = sigmoid(beta_raw), and S the V x K state:
+//
+//   D = S Diag(e^g)                     decay
+//   u = D k-hat                         (V)
+//   S = D + beta (v - u) k-hat^T        delta update with the token's own gate
+//   o = scale * S q-hat                 read-out from the updated state
+//
+// A sequence with no token leaves its state unchanged, and the state is still written
+// back: a flagged paged slot round-trips bit for bit and an unflagged one becomes zero,
+// as in the chunked path.
+//
+// It is bound by the state traffic (one read and one write of V x K elements per
+// sequence and head), so it is a single pass over the state rows in fp32: a workgroup
+// per (sequence, head); wave w owns value rows 32w .. 32w+31, four rows at a time with
+// sixteen lanes per row and eight keys per lane (one or two 16-byte accesses). Every
+// row's loads are issued before any of its arithmetic, the rows stay packed at the
+// storage dtype until they are used, and the two row reductions (u and o) are 16-lane
+// butterflies.
+
+#include <hip/hip_ext.h>
+#include <hip/hip_runtime.h>
+
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+namespace {
+
+constexpr int kRowsPerWave = 32;
+constexpr int kIters = kRowsPerWave / 4;  // four rows per wave per iteration
+
+// Sum over the 16 lanes of a row group (lanes 16r .. 16r+15).
+__device__ __forceinline__ float sum16(float x) {
+  x += __shfl_xor(x, 1);
+  x += __shfl_xor(x, 2);
+  x += __shfl_xor(x, 4);
+  x += __shfl_xor(x, 8);
+  return x;
+}
+
+__device__ __forceinline__ float sigmoid(float x) { return 1.0f / (1.0f + __expf(-x)); }
+
+// Eight state elements of one row, as stored: 32 bytes of fp32 or 16 bytes of fp16/bf16,
+// each moved with 16-byte accesses.
+template <int SDT>
+struct Row8 {
+  uint4 w[SDT == kF32 ? 2 : 1];
+};
+
+template <int SDT>
+__device__ __forceinline__ Row8<SDT> load_row8(const void* plane, size_t off) {
+  Row8<SDT> r;
+  const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(plane) + off * elem_size<SDT>());
+#pragma unroll
+  for (int i = 0; i < (SDT == kF32 ? 2 : 1); ++i) r.w[i] = src[i];
+  return r;
+}
+
+template <int SDT>
+__device__ __forceinline__ float row8_get(const Row8<SDT>& r, int j) {
+  if constexpr (SDT == kF32) {
+    const uint32_t x = j < 4 ? (&r.w[0].x)[j] : (&r.w[1].x)[j - 4];
+    return __uint_as_float(x);
+  } else {
+    const uint32_t x = (&r.w[0].x)[j >> 1];
+    const uint16_t b = (j & 1) ? (uint16_t)(x >> 16) : (uint16_t)(x & 0xffffu);
+    if constexpr (SDT == kF16) return (float)__builtin_bit_cast(_Float16, b);
+    else return __uint_as_float((uint32_t)b << 16);
+  }
+}
+
+template <int SDT>
+__device__ __forceinline__ void store_row8(void* plane, size_t off, const float* x) {
+  uint4* dst = reinterpret_cast<uint4*>(reinterpret_cast<char*>(plane) + off * elem_size<SDT>());
+  if constexpr (SDT == kF32) {
+    dst[0] = uint4{__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]), __float_as_uint(x[3])};
+    dst[1] = uint4{__float_as_uint(x[4]), __float_as_uint(x[5]), __float_as_uint(x[6]), __float_as_uint(x[7])};
+  } else {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint16_t lo, hi;
+      if constexpr (SDT == kF16) {
+        lo = __builtin_bit_cast(uint16_t, (_Float16)x[2 * i]);
+        hi = __builtin_bit_cast(uint16_t, (_Float16)x[2 * i + 1]);
+      } else {
+        lo = __builtin_bit_cast(uint16_t, to_bf16(x[2 * i]));
+        hi = __builtin_bit_cast(uint16_t, to_bf16(x[2 * i + 1]));
+      }
+      w[i] = (uint32_t)lo | ((uint32_t)hi << 16);
+    }
+    dst[0] = uint4{w[0], w[1], w[2], w[3]};
+  }
+}
+
+template <int SDT, bool GF32>
+__global__ __launch_bounds__(256) void decode_kernel(Plan p) {
+  const int n = blockIdx.x / p.H;
+  const int h = blockIdx.x - n * p.H;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int rg = lane >> 4;       // row of the group of four
+  const int k0 = 8 * (lane & 15);  // this lane's eight keys
+  const int t0 = __builtin_amdgcn_readfirstlane(p.d_cu[n]);
+  const bool has_token = __builtin_amdgcn_readfirstlane(p.d_cu[n + 1]) > t0;
+
+  // State rows of this wave, all loads first, kept as stored until used.
+  const void* in_plane = state_in_plane<SDT>(p, n, h);
+  Row8<SDT> raw[kIters];
+#pragma unroll
+  for (int i = 0; i < kIters; ++i) {
+    const size_t off = (size_t)(kRowsPerWave * wave + 4 * i + rg) * kHead + k0;
+    if (in_plane) raw[i] = load_row8<SDT>(in_plane, off);
+    else raw[i] = Row8<SDT>{};
+  }
+  void* out_plane = state_out_plane<SDT>(p, n, h);
+
+  float o_rows[kIters];
+  if (has_token) {
+    const size_t tok = ((size_t)t0 * p.H + h) * kHead;
+    // q, k (bf16), the raw gate, beta and this lane's value rows.
+    const uint4 qw = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(p.q) + tok + k0);
+    const uint4 kw = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(p.k) + tok + k0);
+    float gr[8];
+    if constexpr (GF32) {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(p.g_raw) + tok + k0);
+      const f32x4 b = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(p.g_raw) + tok + k0 + 4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        gr[j] = a[j];
+        gr[4 + j] = b[j];
+      }
+    } else {
+      const uint4 gw = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(p.g_raw) + tok + k0);
+      const uint32_t g32[4] = {gw.x, gw.y, gw.z, gw.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        gr[2 * j] = __uint_as_float(g32[j] << 16);
+        gr[2 * j + 1] = __uint_as_float(g32[j] & 0xffff0000u);
+      }
+    }
+    const size_t bidx = (size_t)t0 * p.H + h;
+    const float braw = p.beta_dtype == kF32 ? reinterpret_cast<const float*>(p.beta_raw)[bidx]
+                                            : bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(p.beta_raw)[bidx]);
+    float vr[kIters];
+#pragma unroll
+    for (int i = 0; i < kIters; ++i)
+      vr[i] = bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(p.v)[tok + kRowsPerWave * wave + 4 * i + rg]);
+
+    const uint32_t q32[4] = {qw.x, qw.y, qw.z, qw.w}, k32[4] = {kw.x, kw.y, kw.z, kw.w};
+    float qh[8], kh[8], eg[8];
+    float sq = 0.f, sk = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      qh[2 * j] = __uint_as_float(q32[j] << 16);
+      qh[2 * j + 1] = __uint_as_float(q32[j] & 0xffff0000u);
+      kh[2 * j] = __uint_as_float(k32[j] << 16);
+      kh[2 * j + 1] = __uint_as_float(k32[j] & 0xffff0000u);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      sq += qh[j] * qh[j];
+      sk += kh[j] * kh[j];
+      eg[j] = __expf(p.lower_bound * sigmoid(gr[j]));
+    }
+    const float rq = rsqrtf(sum16(sq) + 1e-6f) * p.scale;  // scale folded into q-hat
+    const float rk = rsqrtf(sum16(sk) + 1e-6f);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      qh[j] *= rq;
+      kh[j] *= rk;
+    }
+    const float beta = sigmoid(braw);
+
+    // Each row is stored as soon as it is updated.
+#pragma unroll
+    for (int i = 0; i < kIters; ++i) {
+      float d[8];
+      float pu = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        d[j] = row8_get<SDT>(raw[i], j) * eg[j];
+        pu += d[j] * kh[j];
+      }
+      const float c = beta * (vr[i] - sum16(pu));
+      float po = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        d[j] += c * kh[j];
+        po += d[j] * qh[j];
+      }
+      o_rows[i] = sum16(po);
+      if (out_plane) store_row8<SDT>(out_plane, (size_t)(kRowsPerWave * wave + 4 * i + rg) * kHead + k0, d);
+    }
+  } else if (out_plane) {
+    // No token: the state is written back as read (zero when nothing was read).
+#pragma unroll
+    for (int i = 0; i < kIters; ++i) {
+      uint4* dst = reinterpret_cast<uint4*>(reinterpret_cast<char*>(out_plane) +
+                                            ((size_t)(kRowsPerWave * wave + 4 * i + rg) * kHead + k0) * elem_size<SDT>());
+#pragma unroll
+      for (int w = 0; w < (SDT == kF32 ? 2 : 1); ++w) dst[w] = raw[i].w[w];
+    }
+  }
+  if (has_token && (lane & 15) == 0) {
+    __bf16* o = reinterpret_cast<__bf16*>(p.out) + ((size_t)t0 * p.H + h) * kHead + kRowsPerWave * wave + rg;
+#pragma unroll
+    for (int i = 0; i < kIters; ++i) o[4 * i] = to_bf16(o_rows[i]);
+  }
+}
+
+template <int SDT>
+int launch_sdt(const Plan& p, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  const dim3 grid(p.N * p.H);
+  if (p.g_dtype == kF32)
+    hipExtLaunchKernelGGL((decode_kernel<SDT, true>), grid, dim3(256), 0, s, e0, e1, 0, p);
+  else
+    hipExtLaunchKernelGGL((decode_kernel<SDT, false>), grid, dim3(256), 0, s, e0, e1, 0, p);
+  return (int)hipGetLastError();
+}
+
+}  // namespace
+
+int launch_decode(const Plan& p, void* stream, void* start, void* stop) {
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipEvent_t e0 = reinterpret_cast<hipEvent_t>(start), e1 = reinterpret_cast<hipEvent_t>(stop);
+  switch (p.state_dtype) {
+    case kF16: return launch_sdt<kF16>(p, s, e0, e1);
+    case kBF16: return launch_sdt<kBF16>(p, s, e0, e1);
+    default: return launch_sdt<kF32>(p, s, e0, e1);
+  }
+}
+
+}  // namespace kda

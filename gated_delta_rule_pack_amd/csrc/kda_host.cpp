@@ -67,6 +67,7 @@ int rt_launch(void*, int kernel, const void* plan, void* s, void* start, void* s
     case 0: return kda::launch_prep(p, s, start, stop);
     case 1: return kda::launch_scan(p, s, start, stop);
     case 2: return kda::launch_segmap(p, s, start, stop);
+    case 4: return kda::launch_decode(p, s, start, stop);
     default: return kda::launch_segcombine(p, s, start, stop);
   }
 }
@@ -103,6 +104,12 @@ int64_t count_chunks(const int32_t* cu, int N) {
   int64_t n = 0;
   for (int i = 0; i < N; ++i) n += (cu[i + 1] - cu[i] + kChunk - 1) / kChunk;
   return n;
+}
+
+int32_t max_seq_len(const int32_t* cu, int N) {
+  int32_t m = 0;
+  for (int i = 0; i < N; ++i) m = std::max(m, cu[i + 1] - cu[i]);
+  return m;
 }
 
 int64_t max_seq_chunks(const int32_t* cu, int N) {
@@ -266,6 +273,7 @@ struct kda_ctx {
   kda_runtime rt{};
   int dv_split_override = 0;  // tuning only (KDA_DV_SPLIT), 0 = policy
   int seg_len_override = -1;  // tuning only (KDA_SEG_LEN), -1 = policy, 0 = never segment
+  bool decode_off = false;    // testing only (KDA_DECODE=0): one-token calls take the chunked path
   bool profiling = false;
   std::vector<ProfileMarks> marks;       // recorded, not yet read
   std::vector<ProfileMarks> marks_free;  // reusable
@@ -554,6 +562,7 @@ kda_status kda_ctx_create_with_runtime(const kda_runtime* rt, int cu_count, kda_
     const int v = std::atoi(e);
     if (v == 1 || v == 2 || v == 4 || v == 8) ctx->dv_split_override = v;
   }
+  if (const char* e = std::getenv("KDA_DECODE")) ctx->decode_off = e[0] == '0';
   if (const char* e = std::getenv("KDA_SEG_LEN")) {
     const int v = std::atoi(e);
     if (v == 0 || v >= kda::kSegMin) ctx->seg_len_override = v;
@@ -646,6 +655,7 @@ kda_status kda_chunk_fwd(kda_ctx* ctx, const kda_fwd_args* a, void* ws, size_t w
     if (!bounds_ok(cu, a->N, a->T)) return KDA_ERR_INVALID_ARG;
   }
 
+  const bool decode = max_seq_len(cu, a->N) <= 1 && !ctx->decode_off;
   int seg_len = seg_len_for(a->N, a->H, max_seq_chunks(cu, a->N));
   if (ctx->seg_len_override >= 0 && (int64_t)a->N * a->H <= 96) seg_len = ctx->seg_len_override;
   CacheEntry* e = nullptr;
@@ -720,13 +730,19 @@ kda_status kda_chunk_fwd(kda_ctx* ctx, const kda_fwd_args* a, void* ws, size_t w
     }
     pm.prep = p.n_chunks > 0;
   }
-  if (p.n_chunks > 0 && rt.launch(rt.user, 0, &p, stream, pm.ev[0], pm.ev[1])) return hip_fail();
-  if (p.n_maps > 0) {
-    if (rt.launch(rt.user, 2, &p, stream, pm.ev[2], nullptr)) return hip_fail();
-    if (rt.launch(rt.user, 3, &p, stream, nullptr, nullptr)) return hip_fail();
+  if (decode) {
+    // Every sequence has at most one token: the fused recurrent step alone.
+    pm.prep = false;
+    if (rt.launch(rt.user, 4, &p, stream, pm.ev[2], prof ? pm.ev[3] : use_ev)) return hip_fail();
+  } else {
+    if (p.n_chunks > 0 && rt.launch(rt.user, 0, &p, stream, pm.ev[0], pm.ev[1])) return hip_fail();
+    if (p.n_maps > 0) {
+      if (rt.launch(rt.user, 2, &p, stream, pm.ev[2], nullptr)) return hip_fail();
+      if (rt.launch(rt.user, 3, &p, stream, nullptr, nullptr)) return hip_fail();
+    }
+    if (rt.launch(rt.user, 1, &p, stream, p.n_maps > 0 ? nullptr : pm.ev[2], prof ? pm.ev[3] : use_ev))
+      return hip_fail();
   }
-  if (rt.launch(rt.user, 1, &p, stream, p.n_maps > 0 ? nullptr : pm.ev[2], prof ? pm.ev[3] : use_ev))
-    return hip_fail();
   if (prof) {
     ctx->marks.push_back(pm);
     if (use_ev && rt.event_record(rt.user, use_ev, stream)) return hip_fail();

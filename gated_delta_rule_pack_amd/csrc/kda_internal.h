@@ -90,5 +90,6 @@ int launch_prep(const Plan& p, void* stream, void* start, void* stop);
 int launch_scan(const Plan& p, void* stream, void* start, void* stop);
 int launch_segmap(const Plan& p, void* stream, void* start, void* stop);
 int launch_segcombine(const Plan& p, void* stream, void* start, void* stop);
+int launch_decode(const Plan& p, void* stream, void* start, void* stop);
 
 }  // namespace kda

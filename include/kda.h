@@ -143,7 +143,8 @@ typedef struct kda_runtime {
   int (*device_alloc)(void* user, void** ptr, size_t bytes);
   int (*device_free)(void* user, void* ptr);
   /* kernel: 0 = prep (only when the call has chunks), 1 = scan, 2 = segment maps,
-   * 3 = segment combine (2 and 3 only for a segmented call, between prep and scan). plan
+   * 3 = segment combine (2 and 3 only for a segmented call, between prep and scan),
+   * 4 = decode (alone, when no sequence of the call has more than one token). plan
    * is internal launch data, opaque to the runtime. start and stop, when not NULL, are
    * events the launch itself records when the kernel starts and when it completes
    * (hipExtLaunchKernel), with no separate marker in the stream. */

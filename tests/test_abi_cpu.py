@@ -414,7 +414,7 @@ def test_profiling_attaches_timing_events_to_launches(lib, fake):
     b, _, _ = _valid_args(bufs, T=0, N=2, cu=np.array([0, 0, 0], np.int32), paged=True)
     fake.launches.clear()
     assert _call(lib, fake, b) == _lib.KDA_OK
-    assert fake.launches == [(1, 0x10)]
+    assert fake.launches == [(4, 0x10)]  # no sequence longer than one token: decode alone
     per_call, n = (ctypes.c_float * 4)(), ctypes.c_int64()
     assert lib.kda_profile_calls(fake.ctx, per_call, 4, ctypes.byref(n)) == _lib.KDA_OK
     assert n.value == 2 and list(per_call)[:2] == [1.0, 1.0]  # first kernel start to scan end
@@ -424,6 +424,19 @@ def test_profiling_attaches_timing_events_to_launches(lib, fake):
     assert lib.kda_profile_read(fake.ctx, ctypes.byref(prep), ctypes.byref(scan), ctypes.byref(calls)) == _lib.KDA_OK
     assert calls.value == 2 and prep.value == 1.0 and scan.value == 2.0
     assert lib.kda_profile_enable(fake.ctx, 0) == _lib.KDA_OK
+
+
+def test_one_token_calls_take_the_decode_kernel(lib, fake):
+    """Calls whose sequences have at most one token launch the decode kernel alone; a
+    single longer sequence brings back prep and scan."""
+    bufs = FakeBufs()
+    a, _, _ = _valid_args(bufs, T=3, N=4, cu=np.array([0, 1, 1, 2, 3], np.int32), paged=True)
+    assert _call(lib, fake, a) == _lib.KDA_OK
+    assert fake.launches == [(4, 0x10)]
+    fake.launches.clear()
+    b, _, _ = _valid_args(bufs, T=3, N=2, cu=np.array([0, 1, 3], np.int32), paged=True)
+    assert _call(lib, fake, b) == _lib.KDA_OK
+    assert fake.launches == [(0, 0x10), (1, 0x10)]
 
 
 def _segments_reference(cu, L):
