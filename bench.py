@@ -1,8 +1,9 @@
 #!/usr/bin/env python3
 """Benchmark chunkwise KDA prefill on one MI355X.
 
-One step = one ``kda_chunk_fwd`` call (metadata lookup, prep kernel, scan kernel) over
-one batch of synthetic input already resident in HBM. The default workload is the
+One step = one ``kda_chunk_fwd`` call (metadata lookup, prep kernel, scan kernel; or the
+decode kernel alone when no sequence has more than one token) over one batch of
+synthetic input already resident in HBM. The default workload is the
 1 x 4096-token, 12-head call with a paged fp32 state pool (the per-GPU Kimi-K3 serving
 shape); ``--workload`` selects the other shapes.
 
@@ -145,6 +146,7 @@ def algorithmic_bytes(wl, kernel: str, n_chunks: int):
           (4 / 2 B) per valid token-head; writes one 35328-byte record per chunk-head.
     scan: reads each chunk-head record once; writes 256 B of output per token-head;
           reads (when the flag is set) and writes one V x K state per sequence-head.
+    decode: the one-token kernel moves exactly the method's own bytes (as ``call``).
     call: the method's own bytes: q, k, v, raw gate, raw beta, out per token-head plus the
           state read/write, no intermediates.
     """
@@ -241,18 +243,24 @@ def main():
     stream = torch.cuda.current_stream(dev)
 
     # Input sets resident in HBM, rotated so the caches cannot hold them between steps.
+    # Each set has its own state pool: the state a call reads and writes (one V x K
+    # block per sequence and head) counts toward the set's footprint.
+    s_elem = {"f32": 4, "f16": 2, "bf16": 2}[wl.state_dtype]
     per_set = sum(t.numel() * t.element_size() for t in (wl.q, wl.k, wl.v, wl.g_raw, wl.beta_raw)) + \
-        wl.v.numel() * 2
+        wl.v.numel() * 2 + (2 * wl.N * wl.H * 128 * 128 * s_elem if wl.state_mode == "paged" else 0)
     n_rot = args.rotate or max(1, min(8, (512 << 20) // per_set + 1))
     base = {n: getattr(wl, n).to(dev) for n in ("q", "k", "v", "g_raw", "beta_raw")}
     cu_d = wl.cu_seqlens.to(dev)
     cu_h = wl.cu_seqlens.clone()
-    state = {}
+    pools = [{}]
     if wl.state_mode == "paged":
-        storage = wl.state_storage.to(dev)
-        state = dict(state_cache=storage.as_strided((wl.num_slots, wl.H, 128, 128),
-                                                    (wl.state_stride0, 128 * 128, 128, 1)),
-                     state_indices=wl.state_indices.to(dev), has_initial_state=wl.has_initial_state.to(dev))
+        idx_d, flag_d = wl.state_indices.to(dev), wl.has_initial_state.to(dev)
+        pools = []
+        for _ in range(n_rot):
+            storage = wl.state_storage.to(dev)
+            pools.append(dict(state_cache=storage.as_strided((wl.num_slots, wl.H, 128, 128),
+                                                             (wl.state_stride0, 128 * 128, 128, 1)),
+                              state_indices=idx_d, has_initial_state=flag_d))
     # Bounds sets: the workload's own, or (--rotate-bounds K) K seeded permutations of its
     # sequence lengths, so that every call misses the metadata cache (64 entries).
     bounds = [(cu_d, cu_h)]
@@ -274,7 +282,7 @@ def main():
         s = inputs[i % n_rot]
         b_d, b_h = bounds[i % len(bounds)]
         a = kda.make_args(s["q"], s["k"], s["v"], s["g_raw"], s["beta_raw"], b_d, cu_seqlens_cpu=b_h,
-                          scale=wl.scale, lower_bound=wl.lower_bound, out=s["out"], **state)
+                          scale=wl.scale, lower_bound=wl.lower_bound, out=s["out"], **pools[i % len(pools)])
         rc = lib.kda_chunk_fwd_validate(ctypes.byref(a))
         if rc != _lib.KDA_OK:
             raise kda.KDAError(rc, "validate")
@@ -321,7 +329,10 @@ def main():
     value = tokens / (ms_step * 1e-3)
 
     n_chunks = int(stats["last_n_chunks"])
-    k_us = {"prep": 1e3 * prep_ms / max(ncalls, 1), "scan": 1e3 * scan_ms / max(ncalls, 1)}
+    if stats["last_path"] == 1:  # one-token call: the decode kernel alone
+        k_us = {"decode": 1e3 * scan_ms / max(ncalls, 1)}
+    else:
+        k_us = {"prep": 1e3 * prep_ms / max(ncalls, 1), "scan": 1e3 * scan_ms / max(ncalls, 1)}
     dom = max(k_us, key=k_us.get)
     ab = algorithmic_bytes(wl, dom, n_chunks)
     achieved = ab / (k_us[dom] * 1e-6) / 1e9

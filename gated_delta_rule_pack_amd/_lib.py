@@ -56,6 +56,7 @@ class Stats(Structure):
         ("blocking_syncs", c_uint64), ("d2h_reads", c_uint64), ("h2d_uploads", c_uint64),
         ("last_dv_split", c_int32), ("last_ref_block", c_int32), ("last_n_chunks", c_int64),
         ("last_seg_len", c_int32), ("last_n_segments", c_int32),
+        ("last_path", c_int32), ("reserved", c_int32),
     ]
 
     def as_dict(self):
@@ -141,6 +142,10 @@ def load() -> ctypes.CDLL:
     lib.kda_fwd_args_size.argtypes = []
     if lib.kda_fwd_args_size() != ctypes.sizeof(FwdArgs):
         raise ImportError("kda_fwd_args layout mismatch between include/kda.h and the binding")
+    lib.kda_stats_size.restype = c_size_t
+    lib.kda_stats_size.argtypes = []
+    if lib.kda_stats_size() != ctypes.sizeof(Stats):
+        raise ImportError("kda_stats layout mismatch between include/kda.h and the binding")
     _lib = lib
     return lib
 
@@ -154,6 +159,7 @@ EXPORTS = [
     "kda_ctx_create", "kda_ctx_create_with_runtime", "kda_ctx_destroy",
     "kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd_validate", "kda_chunk_fwd",
     "kda_prepare_chunk_indices", "kda_dv_split", "kda_seg_len", "kda_ref_block", "kda_fwd_args_size",
+    "kda_stats_size",
     "kda_status_str", "kda_get_stats", "kda_reset_stats", "kda_profile_enable", "kda_profile_read",
     "kda_profile_calls",
 ]

@@ -753,6 +753,7 @@ kda_status kda_chunk_fwd(kda_ctx* ctx, const kda_fwd_args* a, void* ws, size_t w
   ctx->stats.last_n_chunks = e->meta.n_chunks;
   ctx->stats.last_seg_len = e->meta.seg_len;
   ctx->stats.last_n_segments = e->meta.n_seg;
+  ctx->stats.last_path = decode ? 1 : 0;
   return KDA_OK;
 }
 
@@ -800,5 +801,6 @@ kda_status kda_profile_calls(kda_ctx* ctx, float* call_ms, int64_t cap, int64_t*
 }
 
 size_t kda_fwd_args_size(void) { return sizeof(kda_fwd_args); }
+size_t kda_stats_size(void) { return sizeof(kda_stats); }
 
 }  // extern "C"

@@ -115,6 +115,8 @@ typedef struct kda_stats {
   int64_t last_n_chunks;   /* chunks (over all sequences) in the last call */
   int32_t last_seg_len;    /* segment length (chunks) of the last call's scan, 0 = unsegmented */
   int32_t last_n_segments; /* segments (over all sequences) in the last call */
+  int32_t last_path;       /* kernels of the last call: 0 = prep + scan, 1 = decode */
+  int32_t reserved;        /* zero */
 } kda_stats;
 
 typedef struct kda_ctx kda_ctx;
@@ -215,9 +217,11 @@ int32_t kda_ref_block(float lower_bound);
 
 /* Per-kernel timing, off by default. While enabled, each kda_chunk_fwd attaches timing
  * events to its kernel launches (start and end of prep; start of the first scan-phase
- * kernel and end of the scan), so the durations are the kernels' own, with no marker in
- * the stream. kda_profile_read waits for the recorded events, adds up the prep and scan
- * durations in milliseconds, reports how many calls they cover, and clears them.
+ * kernel and end of the scan; for a decode call, start and end of the decode kernel), so
+ * the durations are the kernels' own, with no marker in the stream. kda_profile_read
+ * waits for the recorded events, adds up the prep and scan durations in milliseconds (a
+ * decode call adds nothing to prep and its decode kernel to scan), reports how many
+ * calls they cover, and clears them.
  * kda_profile_calls (call it before kda_profile_read) writes, in call order, up to cap
  * per-call durations in milliseconds, from the start of the call's first kernel to the
  * end of its scan, sets *n to the number of recorded calls and clears nothing.
@@ -227,8 +231,10 @@ kda_status kda_profile_enable(kda_ctx* ctx, int enable);
 kda_status kda_profile_read(kda_ctx* ctx, double* prep_ms, double* scan_ms, int64_t* calls);
 kda_status kda_profile_calls(kda_ctx* ctx, float* call_ms, int64_t cap, int64_t* n);
 
-/* sizeof(kda_fwd_args), so a binding can check its mirror of the struct. */
+/* sizeof(kda_fwd_args) and sizeof(kda_stats), so a binding can check its mirrors of
+ * the structs. */
 size_t kda_fwd_args_size(void);
+size_t kda_stats_size(void);
 
 const char* kda_status_str(kda_status status);
 kda_status kda_get_stats(const kda_ctx* ctx, kda_stats* out);

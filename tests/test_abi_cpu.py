@@ -33,6 +33,7 @@ def test_header_exports_match_library(lib):
     for name in declared:
         assert hasattr(lib, name), name
     assert lib.kda_fwd_args_size() == ctypes.sizeof(_lib.FwdArgs)
+    assert lib.kda_stats_size() == ctypes.sizeof(_lib.Stats)
 
 
 def test_status_strings(lib):
@@ -433,10 +434,12 @@ def test_one_token_calls_take_the_decode_kernel(lib, fake):
     a, _, _ = _valid_args(bufs, T=3, N=4, cu=np.array([0, 1, 1, 2, 3], np.int32), paged=True)
     assert _call(lib, fake, a) == _lib.KDA_OK
     assert fake.launches == [(4, 0x10)]
+    assert _stats(lib, fake)["last_path"] == 1
     fake.launches.clear()
     b, _, _ = _valid_args(bufs, T=3, N=2, cu=np.array([0, 1, 3], np.int32), paged=True)
     assert _call(lib, fake, b) == _lib.KDA_OK
     assert fake.launches == [(0, 0x10), (1, 0x10)]
+    assert _stats(lib, fake)["last_path"] == 0
 
 
 def _segments_reference(cu, L):
