@@ -129,3 +129,13 @@ def test_256x1_decode_like_state_bound(state_dtype):
     e_out, e_state = compare(wl, run)
     untouched_slots_bitwise(wl, run)
     _say(f"  out {e_out:.3e} state {e_state:.3e}")
+
+
+@pytest.mark.parametrize("name", ["paged_64x1_H12_f16", "paged_64x1_H12_f32"])
+def test_64x1_decode_step(name):
+    wl = standard(name)
+    _say(f"case {wl.name}")
+    run = run_gpu(wl)
+    e_out, e_state = compare(wl, run)
+    untouched_slots_bitwise(wl, run)
+    _say(f"  out {e_out:.3e} state {e_state:.3e}")
