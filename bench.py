@@ -29,6 +29,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "KDA prefill µs/call + tokens/s, H=12 1×4K/1×16K; % of MFMA/HBM peak"
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 RECORD_BYTES = 35328  # per (head, chunk) workspace record written by prep, read by scan
 
 WORKLOADS = {
@@ -166,6 +167,48 @@ def algorithmic_bytes(wl, kernel: str, n_chunks: int):
     if kernel == "scan":
         return n_chunks * wl.H * RECORD_BYTES + th * 256 + state
     return th * (3 * 256 + g_b + b_b + 256) + state
+
+
+def algorithmic_flops(wl, kernel: str):
+    """Per-launch algorithmic flops of one kernel (per token-head figures at C = 32, K = V = 128).
+
+    prep: the four chunk-local products A, P, W and U, 2 x 32 x 128 each per token-head.
+    scan: W S^T, Q~ S^T and Delta^T K^ (2 x 128 x 128 each) plus P Delta (2 x 32 x 128).
+    decode: the token recurrence itself: decay, S k^, the rank-one update and S q^, 7 x 128 x 128.
+    call: prep + scan, or decode.
+    """
+    th = wl.T * wl.H
+    per = {"prep": 4 * 2 * 32 * 128, "scan": 3 * 2 * 128 * 128 + 2 * 32 * 128, "decode": 7 * 128 * 128}
+    per["call"] = per["prep"] + per["scan"]
+    return th * per[kernel]
+
+
+def attainable_peaks(dev):
+    """Live attainable peaks on this part: a plain 512 MiB device copy and a bf16 GEMM loop."""
+    import torch
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps * 1e-3
+
+    src = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    t_copy = timed(lambda: dst.copy_(src), 10)
+    del src, dst
+    n = 8192
+    x = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    y = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    t_gemm = timed(lambda: torch.mm(x, y), 10)
+    return {"copy_GBps": round(2 * (512 << 20) / t_copy / 1e9, 1),
+            "gemm_bf16_TFLOPs": round(2 * n ** 3 / t_gemm / 1e12, 1),
+            "how": "512 MiB device-to-device copy; 8192^3 bf16 torch.mm (hipBLASLt), 10 reps each"}
 
 
 def copy_calibration(mib: int, steps: int, warmup: int):
@@ -340,12 +383,19 @@ def main():
     achieved = ab / (k_us[dom] * 1e-6) / 1e9
     traffic = traffic_from_profiles(dom, args.workload)
     call_bytes = algorithmic_bytes(wl, "call", n_chunks)
+    flops = algorithmic_flops(wl, dom)
+    call_flops = algorithmic_flops(wl, "decode" if dom == "decode" else "call")
     roofline = {
         "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
         "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
         "kernel": f"kda_{dom}", "kernel_us": round(k_us[dom], 2), "algorithmic_bytes": int(ab),
         "call_algorithmic_bytes": int(call_bytes),
         "call_frac": round(call_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "kernel_tflops": round(flops / (k_us[dom] * 1e-6) / 1e12, 2),
+        "kernel_mfma_frac": round(flops / (k_us[dom] * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+        "call_tflops": round(call_flops / (ms_step * 1e-3) / 1e12, 2),
+        "call_mfma_frac": round(call_flops / (ms_step * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+        "attainable": attainable_peaks(dev),
     }
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
