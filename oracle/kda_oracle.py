@@ -30,6 +30,13 @@ Readings where the pages say nothing (each listed with its reason in the design 
 * The gate has no further terms (no per-head A_log / dt_bias / softplus); a caller
   folds any affine pre-transform into ``g_raw``.
 * An empty sequence's final state equals its initial state and is written back.
+* Grouped value heads (GVA, named for the default pipeline in aiter PR 5754,
+  Technical Details): when q and k carry fewer heads (H_qk) than v (H), value head h
+  reads q/k head ``h // (H / H_qk)``, i.e. each q/k head serves a run of consecutive
+  value heads, as ``repeat_interleave`` along the head axis would lay them out.
+* K-first state (same passage; the final-state shape switch between ``(N, H, V, K)``
+  and ``(N, H, K, V)`` in the code under review on aiter PR 5249): a stored plane
+  ``[K, V]`` is the transpose of the V-first ``[V, K]`` one; the recurrence is unchanged.
 
 Chunk numbering (aiter PR 6912, Changes and Tests): chunks are numbered by their
 sequence's position in ``cu_seqlens``; the reference for that numbering is a
@@ -82,13 +89,14 @@ def kda_sequence(q, k, v, g_raw, beta_raw, S0, scale, lower_bound, eps=L2_EPS):
 def kda_forward(
     q, k, v, g_raw, beta_raw, cu_seqlens, *, scale, lower_bound,
     initial_state=None, state_cache=None, state_indices=None, has_initial_state=None,
-    eps=L2_EPS, seqs=None,
+    state_k_first=False, eps=L2_EPS, seqs=None,
 ):
     """Whole-call oracle over a packed varlen batch.
 
     Arrays are float64 numpy (exact upcasts of the stored values):
-    q, k, g_raw ``[T, H, K]``; v ``[T, H, V]``; beta_raw ``[T, H]``;
-    cu_seqlens ``[N+1]`` ints.
+    q, k ``[T, H_qk, K]``; v ``[T, H, V]``; g_raw ``[T, H, K]``; beta_raw ``[T, H]``;
+    cu_seqlens ``[N+1]`` ints. H_qk divides H; value head h reads q/k head
+    ``h // (H / H_qk)`` (H_qk = H: one q/k head per value head).
 
     State, one mode at a time:
       * dense: ``initial_state [N, H, V, K]`` (None means zero);
@@ -96,16 +104,28 @@ def kda_forward(
         ``has_initial_state [N]``; a false flag starts from zero and the slot is
         not read;
       * neither: zero initial state.
+    With ``state_k_first`` every stored plane is ``[K, V]`` instead of ``[V, K]``.
 
     ``seqs`` restricts the work to a subset of sequence ids (for sampled checks).
 
     Returns ``(out, finals)``: ``out [T, H, V]`` (rows of sequences outside ``seqs``
-    are NaN) and ``finals`` a dict ``seq -> [H, V, K]`` final state.
+    are NaN) and ``finals`` a dict ``seq -> final state``, laid out like the stored
+    state: ``[H, V, K]``, or ``[H, K, V]`` with ``state_k_first``.
     """
     cu = [int(x) for x in np.asarray(cu_seqlens).tolist()]
     N = len(cu) - 1
-    T, H, K = q.shape
-    V = v.shape[2]
+    T, H, V = v.shape
+    H_qk, K = q.shape[1], q.shape[2]
+    if H % H_qk != 0 or k.shape[1] != H_qk:
+        raise ValueError("q and k must have the same head count, dividing v's")
+    if H_qk != H:  # each q/k head serves H / H_qk consecutive value heads
+        q = np.repeat(q, H // H_qk, axis=1)
+        k = np.repeat(k, H // H_qk, axis=1)
+
+    def to_math(plane):  # stored plane(s) -> [.., V, K]
+        plane = np.asarray(plane, dtype=np.float64)
+        return np.swapaxes(plane, -1, -2) if state_k_first else plane
+
     out = np.full((T, H, V), np.nan, dtype=np.float64)
     finals = {}
     if initial_state is not None and state_cache is not None:
@@ -114,17 +134,17 @@ def kda_forward(
         a, b = cu[n], cu[n + 1]
         if state_cache is not None:
             if bool(has_initial_state[n]):
-                S0 = np.asarray(state_cache[int(state_indices[n])], dtype=np.float64)
+                S0 = to_math(state_cache[int(state_indices[n])])
             else:
                 S0 = np.zeros((H, V, K))
         elif initial_state is not None:
-            S0 = np.asarray(initial_state[n], dtype=np.float64)
+            S0 = to_math(initial_state[n])
         else:
             S0 = np.zeros((H, V, K))
         o, S = kda_sequence(q[a:b], k[a:b], v[a:b], g_raw[a:b], beta_raw[a:b], S0,
                             scale, lower_bound, eps)
         out[a:b] = o
-        finals[n] = S
+        finals[n] = np.ascontiguousarray(np.swapaxes(S, -1, -2)) if state_k_first else S
     return out, finals
 
 

@@ -117,6 +117,63 @@ def test_brute_force_varlen_with_empty_and_paged():
     assert np.array_equal(finals[1][0], pool[0, 0])
 
 
+def test_brute_force_grouped_value_heads():
+    """Two q/k heads serving six value heads (three each): value head h reads q/k head
+    h // 3. With H_qk = 2 and groups of 3, h // 3 and h % 3 pick different heads for
+    every h but 0, so a swapped index cannot pass."""
+    rng = np.random.default_rng(21)
+    K, V, L, H, H_qk = 4, 3, 6, 6, 2
+    q = rng.standard_normal((L, H_qk, K))
+    k = rng.standard_normal((L, H_qk, K))
+    v = rng.standard_normal((L, H, V))
+    graw = rng.standard_normal((L, H, K))
+    braw = rng.standard_normal((L, H))
+    S0 = 0.1 * rng.standard_normal((1, H, V, K))
+    cu = np.array([0, L])
+    out, finals = kda_forward(q, k, v, graw, braw, cu, scale=0.5, lower_bound=-5.0, initial_state=S0)
+    for h in range(H):
+        j = h // (H // H_qk)
+        ob, Sb = _brute_force_head(q[:, j], k[:, j], v[:, h], graw[:, h], braw[:, h], S0[0, h], 0.5, -5.0)
+        assert np.max(np.abs(out[:, h] - ob)) <= 1e-12
+        assert np.max(np.abs(finals[0][h] - Sb)) <= 1e-12
+
+
+def test_grouped_heads_must_divide():
+    rng = np.random.default_rng(22)
+    q = rng.standard_normal((2, 4, 4))
+    v = rng.standard_normal((2, 6, 4))
+    with pytest.raises(ValueError):
+        kda_forward(q, q, v, rng.standard_normal((2, 6, 4)), rng.standard_normal((2, 6)), [0, 2],
+                    scale=1.0, lower_bound=-5.0)
+
+
+def test_brute_force_k_first_state():
+    """K-first planes [K, V]: the stored initial state is read as its transpose and the
+    final state is written back transposed; checked against the brute force on a
+    rectangular K != V plane, through a paged pool with mixed flags."""
+    rng = np.random.default_rng(23)
+    K, V, H = 5, 3, 2
+    lens = [4, 0, 5]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    T = int(cu[-1])
+    q, k, v, graw, braw, _ = _rand_case(rng, T, H, K, V)
+    pool = rng.standard_normal((4, H, K, V))  # K-first planes
+    idx = np.array([3, 1, 0])
+    flags = np.array([True, True, False])
+    pool[0] = np.nan  # flag false: must not be read
+    out, finals = kda_forward(q, k, v, graw, braw, cu, scale=0.4, lower_bound=-5.0, state_cache=pool,
+                              state_indices=idx, has_initial_state=flags, state_k_first=True)
+    for n in range(3):
+        a, b = cu[n], cu[n + 1]
+        assert finals[n].shape == (H, K, V)
+        for h in range(H):
+            S0 = pool[idx[n], h].T if flags[n] else np.zeros((V, K))
+            ob, Sb = _brute_force_head(q[a:b, h], k[a:b, h], v[a:b, h], graw[a:b, h], braw[a:b, h], S0, 0.4, -5.0)
+            assert np.allclose(out[a:b, h], ob, rtol=0, atol=1e-12)
+            assert np.allclose(finals[n][h], Sb.T, rtol=0, atol=1e-12)
+    assert np.array_equal(finals[1], pool[1])  # empty sequence: stored plane round-trips
+
+
 # ---------------------------------------------------------------- closed forms
 def test_closed_form_single_token():
     """T=1: o = scale [S0 (e^g * q^) + beta (v - S0 (e^g * k^)) (k^ . q^)]."""
