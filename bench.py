@@ -154,6 +154,7 @@ def algorithmic_bytes(wl, kernel: str, n_chunks: int):
           state read/write, no intermediates.
     """
     th = wl.T * wl.H
+    qk_b = 2 * 256 * wl.H_qk // wl.H  # q and k bytes per token-head (grouped heads share them)
     g_b = wl.g_raw.element_size() * 128
     b_b = wl.beta_raw.element_size()
     s_b = {"f32": 4, "f16": 2, "bf16": 2}[wl.state_dtype] * 128 * 128
@@ -163,10 +164,10 @@ def algorithmic_bytes(wl, kernel: str, n_chunks: int):
     n_write = wl.N if wl.state_mode in ("paged", "dense") else 0
     state = (n_read + n_write) * wl.H * s_b
     if kernel == "prep":
-        return th * (3 * 256 + g_b + b_b) + n_chunks * wl.H * RECORD_BYTES
+        return th * (qk_b + 256 + g_b + b_b) + n_chunks * wl.H * RECORD_BYTES
     if kernel == "scan":
         return n_chunks * wl.H * RECORD_BYTES + th * 256 + state
-    return th * (3 * 256 + g_b + b_b + 256) + state
+    return th * (qk_b + 256 + g_b + b_b + 256) + state
 
 
 def algorithmic_flops(wl, kernel: str):

@@ -113,8 +113,11 @@ def _check_dev(name, t, device):
 
 def make_args(q, k, v, g_raw, beta_raw, cu_seqlens, *, cu_seqlens_cpu=None, scale=None,
               lower_bound=-5.0, initial_state=None, final_state=None, state_cache=None,
-              state_indices=None, has_initial_state=None, out=None) -> _lib.FwdArgs:
-    """Fill a ``kda_fwd_args`` from tensors (no allocation, no checks beyond shapes)."""
+              state_indices=None, has_initial_state=None, out=None, state_k_first=False) -> _lib.FwdArgs:
+    """Fill a ``kda_fwd_args`` from tensors (no allocation, no checks beyond shapes).
+
+    q and k may carry fewer heads than v (grouped value heads): their head count is
+    passed as ``H_qk``. ``state_k_first`` marks every state plane as ``[K, V]``."""
     import torch
     if q.dim() == 4:
         if q.shape[0] != 1:
@@ -123,8 +126,12 @@ def make_args(q, k, v, g_raw, beta_raw, cu_seqlens, *, cu_seqlens_cpu=None, scal
         beta_raw = beta_raw[0]
         if out is not None and out.dim() == 4:
             out = out[0]
-    T, H, K = q.shape
-    V = v.shape[-1]
+    T, H_qk, K = q.shape
+    H, V = v.shape[1], v.shape[2]
+    if tuple(k.shape) != (T, H_qk, K):
+        raise ValueError("q and k must have the same shape")
+    if H_qk > H or H % H_qk != 0:
+        raise ValueError(f"q/k heads ({H_qk}) must divide v heads ({H})")
     N = cu_seqlens.numel() - 1
     for name, t in (("q", q), ("k", k), ("v", v), ("g_raw", g_raw), ("beta_raw", beta_raw)):
         if not t.is_contiguous():
@@ -162,6 +169,8 @@ def make_args(q, k, v, g_raw, beta_raw, cu_seqlens, *, cu_seqlens_cpu=None, scal
         a.state_indices = _ptr(state_indices)
         a.has_initial_state = _ptr(has_initial_state)
     a.out = _ptr(out)
+    a.H_qk = H_qk
+    a.state_k_first = 1 if state_k_first else 0
     return a
 
 
@@ -172,16 +181,19 @@ def workspace_bytes(args: _lib.FwdArgs) -> int:
 def chunk_fwd(q, k, v, g_raw, beta_raw, cu_seqlens, *, cu_seqlens_cpu=None, scale=None,
               lower_bound=-5.0, initial_state=None, output_final_state=False, state_cache=None,
               state_indices=None, has_initial_state=None, out=None, workspace=None, stream=None,
-              context=None):
+              context=None, state_k_first=False):
     """Chunkwise KDA prefill forward on the current (or given) stream.
 
     q, k, v: bf16 ``[1, T, H, 128]``; g_raw: ``[1, T, H, 128]`` fp32/bf16; beta_raw:
     ``[1, T, H]`` fp32/bf16; cu_seqlens: int32 ``[N+1]`` on the device, with an optional
-    CPU copy ``cu_seqlens_cpu`` (then no synchronising call happens).
+    CPU copy ``cu_seqlens_cpu`` (then no synchronising call happens). q and k may have
+    ``H_qk`` heads dividing H (grouped value heads: value head h reads q/k head
+    ``h // (H // H_qk)``).
 
     State: dense ``initial_state [N, H, V, K]`` (fp32/fp16/bf16) with
     ``output_final_state``, or a paged ``state_cache [slots, H, V, K]`` (padded stride(0)
     allowed) with ``state_indices`` int32 ``[N]`` and ``has_initial_state`` bool ``[N]``.
+    With ``state_k_first`` every state plane is ``[K, V]`` instead.
 
     Returns ``(out, final_state)``; ``final_state`` is None in paged mode (the pool is
     updated in place) and when not requested. ``context`` defaults to the device's
@@ -199,14 +211,15 @@ def chunk_fwd(q, k, v, g_raw, beta_raw, cu_seqlens, *, cu_seqlens_cpu=None, scal
         out = torch.empty_like(v)
     final_state = None
     if output_final_state and state_cache is None:
-        T, H, K = q.shape[-3:]
+        K = q.shape[-1]
+        H, V = v.shape[-2:]
         N = cu_seqlens.numel() - 1
         dt = initial_state.dtype if initial_state is not None else torch.float32
-        final_state = torch.empty((N, H, v.shape[-1], K), dtype=dt, device=device)
+        final_state = torch.empty((N, H, K, V) if state_k_first else (N, H, V, K), dtype=dt, device=device)
     a = make_args(q, k, v, g_raw, beta_raw, cu_seqlens, cu_seqlens_cpu=cu_seqlens_cpu, scale=scale,
                   lower_bound=lower_bound, initial_state=initial_state, final_state=final_state,
                   state_cache=state_cache, state_indices=state_indices,
-                  has_initial_state=has_initial_state, out=out)
+                  has_initial_state=has_initial_state, out=out, state_k_first=state_k_first)
     lib = _lib.load()
     rc = lib.kda_chunk_fwd_validate(ctypes.byref(a))
     if rc != _lib.KDA_OK:

@@ -47,6 +47,7 @@ class FwdArgs(Structure):
         ("num_slots", c_int64), ("state_cache_stride0", c_int64),
         ("state_indices", c_void_p), ("has_initial_state", c_void_p),
         ("out", c_void_p),
+        ("H_qk", c_int32), ("state_k_first", c_int32),
     ]
 
 

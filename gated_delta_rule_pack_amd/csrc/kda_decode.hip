@@ -107,6 +107,7 @@ __global__ __launch_bounds__(256) void decode_kernel(Plan p) {
   const int lane = threadIdx.x & 63;
   const int rg = lane >> 4;       // row of the group of four
   const int k0 = 8 * (lane & 15);  // this lane's eight keys
+  const int hqk = __builtin_amdgcn_readfirstlane(h / p.group);  // q/k head of value head h
   const int t0 = __builtin_amdgcn_readfirstlane(p.d_cu[n]);
   const bool has_token = __builtin_amdgcn_readfirstlane(p.d_cu[n + 1]) > t0;
 
@@ -124,9 +125,10 @@ __global__ __launch_bounds__(256) void decode_kernel(Plan p) {
   float o_rows[kIters];
   if (has_token) {
     const size_t tok = ((size_t)t0 * p.H + h) * kHead;
+    const size_t tqk = ((size_t)t0 * p.H_qk + hqk) * kHead;
     // q, k (bf16), the raw gate, beta and this lane's value rows.
-    const uint4 qw = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(p.q) + tok + k0);
-    const uint4 kw = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(p.k) + tok + k0);
+    const uint4 qw = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(p.q) + tqk + k0);
+    const uint4 kw = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(p.k) + tqk + k0);
     float gr[8];
     if constexpr (GF32) {
       const f32x4 a = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(p.g_raw) + tok + k0);
@@ -215,13 +217,125 @@ __global__ __launch_bounds__(256) void decode_kernel(Plan p) {
   }
 }
 
+// K-first planes [K][V]. Wave w owns value columns 32w .. 32w+31; lane (ko = lane & 15,
+// vo = lane >> 4) holds S[k][v] for keys k = 16i + ko (i = 0..7) and the eight columns
+// v = 32w + 8vo .. 32w + 8vo + 7, one or two 16-byte accesses per key. The sums over k
+// (u and o) run over the lane's eight keys, then over the 16 lanes of its group, which
+// hold all 128 keys of the same columns.
+template <int SDT, bool GF32>
+__global__ __launch_bounds__(256) void decode_kfirst_kernel(Plan p) {
+  const int n = blockIdx.x / p.H;
+  const int h = blockIdx.x - n * p.H;
+  const int hqk = __builtin_amdgcn_readfirstlane(h / p.group);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int ko = lane & 15;
+  const int v0 = kRowsPerWave * wave + 8 * (lane >> 4);
+  const int t0 = __builtin_amdgcn_readfirstlane(p.d_cu[n]);
+  const bool has_token = __builtin_amdgcn_readfirstlane(p.d_cu[n + 1]) > t0;
+
+  const void* in_plane = state_in_plane<SDT>(p, n, h);
+  Row8<SDT> raw[kIters];
+#pragma unroll
+  for (int i = 0; i < kIters; ++i) {
+    if (in_plane) raw[i] = load_row8<SDT>(in_plane, (size_t)(16 * i + ko) * kHead + v0);
+    else raw[i] = Row8<SDT>{};
+  }
+  void* out_plane = state_out_plane<SDT>(p, n, h);
+
+  if (has_token) {
+    const size_t tok = ((size_t)t0 * p.H + h) * kHead;
+    const size_t tqk = ((size_t)t0 * p.H_qk + hqk) * kHead;
+    const uint16_t* q16 = reinterpret_cast<const uint16_t*>(p.q) + tqk;
+    const uint16_t* k16 = reinterpret_cast<const uint16_t*>(p.k) + tqk;
+    float qh[kIters], kh[kIters], eg[kIters];
+    float sq = 0.f, sk = 0.f;
+#pragma unroll
+    for (int i = 0; i < kIters; ++i) {
+      const int kk = 16 * i + ko;
+      qh[i] = bf16_bits_to_f32(q16[kk]);
+      kh[i] = bf16_bits_to_f32(k16[kk]);
+      const float gr = GF32 ? reinterpret_cast<const float*>(p.g_raw)[tok + kk]
+                            : bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(p.g_raw)[tok + kk]);
+      eg[i] = __expf(p.lower_bound * sigmoid(gr));
+      sq += qh[i] * qh[i];
+      sk += kh[i] * kh[i];
+    }
+    const size_t bidx = (size_t)t0 * p.H + h;
+    const float braw = p.beta_dtype == kF32 ? reinterpret_cast<const float*>(p.beta_raw)[bidx]
+                                            : bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(p.beta_raw)[bidx]);
+    const uint4 vw = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(p.v) + tok + v0);
+    const uint32_t v32[4] = {vw.x, vw.y, vw.z, vw.w};
+    const float rq = rsqrtf(sum16(sq) + 1e-6f) * p.scale;  // scale folded into q-hat
+    const float rk = rsqrtf(sum16(sk) + 1e-6f);
+#pragma unroll
+    for (int i = 0; i < kIters; ++i) {
+      qh[i] *= rq;
+      kh[i] *= rk;
+    }
+    const float beta = sigmoid(braw);
+
+    // u = D k-hat for the lane's eight columns.
+    float pu[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < kIters; ++i) {
+      const float w = eg[i] * kh[i];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) pu[j] += row8_get<SDT>(raw[i], j) * w;
+    }
+    float c[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float vj = __uint_as_float((j & 1) ? (v32[j >> 1] & 0xffff0000u) : (v32[j >> 1] << 16));
+      c[j] = beta * (vj - sum16(pu[j]));
+    }
+    // Update, store each key row as soon as it is done, and accumulate o = S q-hat.
+    float po[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < kIters; ++i) {
+      float x[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        x[j] = row8_get<SDT>(raw[i], j) * eg[i] + c[j] * kh[i];
+        po[j] += x[j] * qh[i];
+      }
+      if (out_plane) store_row8<SDT>(out_plane, (size_t)(16 * i + ko) * kHead + v0, x);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) po[j] = sum16(po[j]);
+    if (ko == 0) {
+      uint32_t w[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        w[j] = (uint32_t)__builtin_bit_cast(uint16_t, to_bf16(po[2 * j])) |
+               ((uint32_t)__builtin_bit_cast(uint16_t, to_bf16(po[2 * j + 1])) << 16);
+      *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(p.out) + tok + v0) = uint4{w[0], w[1], w[2], w[3]};
+    }
+  } else if (out_plane) {
+    // No token: the state is written back as read (zero when nothing was read).
+#pragma unroll
+    for (int i = 0; i < kIters; ++i) {
+      uint4* dst = reinterpret_cast<uint4*>(reinterpret_cast<char*>(out_plane) +
+                                            ((size_t)(16 * i + ko) * kHead + v0) * elem_size<SDT>());
+#pragma unroll
+      for (int w = 0; w < (SDT == kF32 ? 2 : 1); ++w) dst[w] = raw[i].w[w];
+    }
+  }
+}
+
 template <int SDT>
 int launch_sdt(const Plan& p, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   const dim3 grid(p.N * p.H);
-  if (p.g_dtype == kF32)
+  if (p.kfirst) {
+    if (p.g_dtype == kF32)
+      hipExtLaunchKernelGGL((decode_kfirst_kernel<SDT, true>), grid, dim3(256), 0, s, e0, e1, 0, p);
+    else
+      hipExtLaunchKernelGGL((decode_kfirst_kernel<SDT, false>), grid, dim3(256), 0, s, e0, e1, 0, p);
+  } else if (p.g_dtype == kF32) {
     hipExtLaunchKernelGGL((decode_kernel<SDT, true>), grid, dim3(256), 0, s, e0, e1, 0, p);
-  else
+  } else {
     hipExtLaunchKernelGGL((decode_kernel<SDT, false>), grid, dim3(256), 0, s, e0, e1, 0, p);
+  }
   return (int)hipGetLastError();
 }
 

@@ -104,6 +104,42 @@ __device__ __forceinline__ size_t elem_size() {
   return SDT == kF32 ? 4 : 2;
 }
 
+template <int SDT>
+__device__ __forceinline__ float load_state1(const void* plane, size_t off) {
+  if constexpr (SDT == kF32) return reinterpret_cast<const float*>(plane)[off];
+  else if constexpr (SDT == kF16) return (float)reinterpret_cast<const _Float16*>(plane)[off];
+  else return (float)reinterpret_cast<const __bf16*>(plane)[off];
+}
+
+template <int SDT>
+__device__ __forceinline__ void store_state1(void* plane, size_t off, float x) {
+  if constexpr (SDT == kF32) reinterpret_cast<float*>(plane)[off] = x;
+  else if constexpr (SDT == kF16) reinterpret_cast<_Float16*>(plane)[off] = (_Float16)x;
+  else reinterpret_cast<__bf16*>(plane)[off] = to_bf16(x);
+}
+
+// State elements (v, k .. k+3) of a plane in either layout: V-first [V][K] holds them
+// in one 16/8-byte run; K-first [K][V] holds them K elements apart (the lanes of a row
+// group, consecutive v, then read consecutive addresses).
+template <int SDT>
+__device__ __forceinline__ f32x4 load_state4_vk(const void* plane, int v, int k, bool kfirst) {
+  if (!kfirst) return load_state4<SDT>(plane, (size_t)v * kHead + k);
+  f32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = load_state1<SDT>(plane, (size_t)(k + i) * kHead + v);
+  return r;
+}
+
+template <int SDT>
+__device__ __forceinline__ void store_state4_vk(void* plane, int v, int k, f32x4 x, bool kfirst) {
+  if (!kfirst) {
+    store_state4<SDT>(plane, (size_t)v * kHead + k, x);
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) store_state1<SDT>(plane, (size_t)(k + i) * kHead + v, x[i]);
+}
+
 // The (sequence n, head h) state plane to read at the start (null: start from zero) and
 // the one to write at the end (null: not written).
 template <int SDT>

@@ -467,6 +467,8 @@ kda_status kda_chunk_fwd_validate(const kda_fwd_args* a) {
   if (a->state_dtype != KDA_F32 && a->state_dtype != KDA_F16 && a->state_dtype != KDA_BF16)
     return KDA_ERR_UNSUPPORTED;
   if (!a->cu_seqlens) return KDA_ERR_INVALID_ARG;
+  if (a->H_qk < 0 || a->H_qk > a->H || (a->H_qk > 0 && a->H % a->H_qk != 0)) return KDA_ERR_INVALID_ARG;
+  if (a->state_k_first != 0 && a->state_k_first != 1) return KDA_ERR_INVALID_ARG;
   if ((int64_t)a->T * a->H > (int64_t)INT32_MAX / kHead) return KDA_ERR_UNSUPPORTED;
   if (a->T > 0) {
     if (!a->q || !a->k || !a->v || !a->g_raw || !a->beta_raw || !a->out) return KDA_ERR_INVALID_ARG;
@@ -668,6 +670,9 @@ kda_status kda_chunk_fwd(kda_ctx* ctx, const kda_fwd_args* a, void* ws, size_t w
   p.T = a->T;
   p.N = a->N;
   p.H = a->H;
+  p.H_qk = a->H_qk > 0 ? a->H_qk : a->H;
+  p.group = a->H / p.H_qk;
+  p.kfirst = a->state_k_first;
   p.n_chunks = (int)e->meta.n_chunks;
   p.scale = a->scale;
   p.lower_bound = a->lower_bound;

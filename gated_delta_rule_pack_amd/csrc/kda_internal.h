@@ -49,6 +49,8 @@ enum DType : int { kF32 = 0, kF16 = 1, kBF16 = 2 };
 // Everything one launch needs; filled by the host orchestration.
 struct Plan {
   int T, N, H, n_chunks;
+  int H_qk, group;  // q/k heads and value heads per q/k head (H = H_qk * group)
+  int kfirst;       // state planes are [K][V] (1) or [V][K] (0)
   float scale, lower_bound;
   int ref_block;  // reference-row block of the bounded decay construction
   int dv_split;   // value-channel split of the scan (8, 4 or 2)

@@ -102,24 +102,29 @@ __device__ __forceinline__ Item item_of(const Plan& p, int item) {
 // elem-byte elements: loads from rows past the sequence fall outside the range and return
 // zero, which is the padding the method needs for q, k and v. The loads never depend on a
 // branch, so the next item's loads stay in flight during compute.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* base, const Item& it, int H, int elem) {
-  const char* b = reinterpret_cast<const char*>(base) + ((size_t)it.t0 * H + it.h) * kHead * elem;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* base, const Item& it, int H, int h, int elem) {
+  const char* b = reinterpret_cast<const char*>(base) + ((size_t)it.t0 * H + h) * kHead * elem;
   const int bytes = it.len > 0 ? (it.len - 1) * H * kHead * elem + kHead * elem : 0;
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(b), (short)0, bytes, kBufWord3);
 }
 
-template <bool GF32>
+// GVA: q and k have H_qk < H heads and value head h reads q/k head h / (H / H_qk). It is
+// a separate instantiation so that the one-to-one case keeps a single set of row offsets
+// (the prep kernel has no registers to spare).
+template <bool GF32, bool GVA>
 __device__ __forceinline__ void load_inputs(const Plan& p, const Item& it, int w, int lane, Inputs& in) {
-  const int H = p.H;
-  const __amdgpu_buffer_rsrc_t rq = rows_rsrc(p.q, it, H, 2), rk = rows_rsrc(p.k, it, H, 2),
-                               rv = rows_rsrc(p.v, it, H, 2), rg = rows_rsrc(p.g_raw, it, H, GF32 ? 4 : 2);
-  const int row2 = H * kHead * 2;  // bytes per token row of a 2-byte tensor
+  const int H = p.H, Hqk = GVA ? p.H_qk : H;
+  const int hqk = GVA ? __builtin_amdgcn_readfirstlane(it.h / p.group) : it.h;
+  const __amdgpu_buffer_rsrc_t rq = rows_rsrc(p.q, it, Hqk, hqk, 2), rk = rows_rsrc(p.k, it, Hqk, hqk, 2),
+                               rv = rows_rsrc(p.v, it, H, it.h, 2), rg = rows_rsrc(p.g_raw, it, H, it.h, GF32 ? 4 : 2);
+  const int row2 = H * kHead * 2;  // bytes per token row of a 2-byte [T][H][128] tensor
   // The whole offset goes in the vector operand: the range check covers only that part.
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int vo = (8 * w + i) * row2 + lane * 4;
-    in.q[i] = __builtin_amdgcn_raw_buffer_load_b32(rq, vo, 0, 0);
-    in.k[i] = __builtin_amdgcn_raw_buffer_load_b32(rk, vo, 0, 0);
+    const int vqk = GVA ? (8 * w + i) * Hqk * kHead * 2 + lane * 4 : vo;
+    in.q[i] = __builtin_amdgcn_raw_buffer_load_b32(rq, vqk, 0, 0);
+    in.k[i] = __builtin_amdgcn_raw_buffer_load_b32(rk, vqk, 0, 0);
     in.v[i] = __builtin_amdgcn_raw_buffer_load_b32(rv, vo, 0, 0);
     if constexpr (GF32) {
       const auto g = __builtin_amdgcn_raw_buffer_load_b64(rg, 2 * vo, 0, 0);
@@ -646,7 +651,7 @@ __device__ void process_item(const Plan& p, const Item& it, const Inputs& in, ch
   }
 }
 
-template <int REF, bool GF32>
+template <int REF, bool GF32, bool GVA>
 __global__ __launch_bounds__(kThreadsPrep, 2) void prep_kernel(Plan p, int n_items) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -658,44 +663,44 @@ __global__ __launch_bounds__(kThreadsPrep, 2) void prep_kernel(Plan p, int n_ite
   // before each item covers only its own inputs.
   Inputs ia, ib;
   Item ta = item_of(p, item), tb;
-  load_inputs<GF32>(p, ta, w, lane, ia);
+  load_inputs<GF32, GVA>(p, ta, w, lane, ia);
   for (;;) {
     tb = item_of(p, min(item + step, n_items - 1));
-    load_inputs<GF32>(p, tb, w, lane, ib);
+    load_inputs<GF32, GVA>(p, tb, w, lane, ib);
     process_item<REF>(p, ta, ia, lds, w, lane);
     item += step;
     if (item >= n_items) break;
     ta = item_of(p, min(item + step, n_items - 1));
-    load_inputs<GF32>(p, ta, w, lane, ia);
+    load_inputs<GF32, GVA>(p, ta, w, lane, ia);
     process_item<REF>(p, tb, ib, lds, w, lane);
     item += step;
     if (item >= n_items) break;
   }
 }
 
-template <int REF, bool GF32>
+template <int REF, bool GF32, bool GVA>
 int launch_ref(const Plan& p, hipStream_t s, int grid, hipEvent_t start, hipEvent_t stop) {
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prep_kernel<REF, GF32>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prep_kernel<REF, GF32, GVA>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes(REF));
     if (e != hipSuccess) return (int)e;
     attr_set = true;
   }
   const int n_items = p.n_chunks * p.H;
-  hipExtLaunchKernelGGL((prep_kernel<REF, GF32>), dim3(min(grid, n_items)), dim3(kThreadsPrep), lds_bytes(REF), s,
+  hipExtLaunchKernelGGL((prep_kernel<REF, GF32, GVA>), dim3(min(grid, n_items)), dim3(kThreadsPrep), lds_bytes(REF), s,
                         start, stop, 0, p, n_items);
   return (int)hipGetLastError();
 }
 
-template <bool GF32>
+template <bool GF32, bool GVA>
 int launch_gate(const Plan& p, hipStream_t s, int grid, hipEvent_t e0, hipEvent_t e1) {
   switch (p.ref_block) {
-    case 16: return launch_ref<16, GF32>(p, s, grid, e0, e1);
-    case 8: return launch_ref<8, GF32>(p, s, grid, e0, e1);
-    case 4: return launch_ref<4, GF32>(p, s, grid, e0, e1);
-    case 2: return launch_ref<2, GF32>(p, s, grid, e0, e1);
-    default: return launch_ref<1, GF32>(p, s, grid, e0, e1);
+    case 16: return launch_ref<16, GF32, GVA>(p, s, grid, e0, e1);
+    case 8: return launch_ref<8, GF32, GVA>(p, s, grid, e0, e1);
+    case 4: return launch_ref<4, GF32, GVA>(p, s, grid, e0, e1);
+    case 2: return launch_ref<2, GF32, GVA>(p, s, grid, e0, e1);
+    default: return launch_ref<1, GF32, GVA>(p, s, grid, e0, e1);
   }
 }
 
@@ -706,7 +711,9 @@ int launch_prep(const Plan& p, void* stream, void* start, void* stop) {
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipEvent_t e0 = reinterpret_cast<hipEvent_t>(start), e1 = reinterpret_cast<hipEvent_t>(stop);
   const int grid = 2 * p.cu_count;  // persistent: two resident workgroups per CU
-  return p.g_dtype == kF32 ? launch_gate<true>(p, s, grid, e0, e1) : launch_gate<false>(p, s, grid, e0, e1);
+  if (p.group > 1)
+    return p.g_dtype == kF32 ? launch_gate<true, true>(p, s, grid, e0, e1) : launch_gate<false, true>(p, s, grid, e0, e1);
+  return p.g_dtype == kF32 ? launch_gate<true, false>(p, s, grid, e0, e1) : launch_gate<false, false>(p, s, grid, e0, e1);
 }
 
 }  // namespace kda

@@ -155,7 +155,9 @@ __device__ __forceinline__ void loader(char* lds, __amdgpu_buffer_rsrc_t rs, int
   }
 }
 
-template <int NTW, int SDT, int KMODE>
+// KF: the caller's state planes are K-first [K][V] (state I/O only; the map mode reads
+// and writes no caller state and uses KF = false).
+template <int NTW, int SDT, int KMODE, bool KF>
 __global__ __launch_bounds__(320, 1) void head_kernel(Plan p, int units, int groups) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   typedef HeadLds<NTW> L;
@@ -197,8 +199,9 @@ __global__ __launch_bounds__(320, 1) void head_kernel(Plan p, int units, int gro
     for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
       for (int tt = 0; tt < 8; ++tt) {
-        const size_t off = (size_t)(16 * (vt0 + nt) + l16) * kHead + 16 * tt + 4 * g4;
-        S[nt][tt] = start ? load_state4<kF32>(start, off) : (in_plane ? load_state4<SDT>(in_plane, off) : zero4());
+        const int v = 16 * (vt0 + nt) + l16, k = 16 * tt + 4 * g4;
+        S[nt][tt] = start ? load_state4<kF32>(start, (size_t)v * kHead + k)
+                          : (in_plane ? load_state4_vk<SDT>(in_plane, v, k, KF) : zero4());
       }
   } else {
 #pragma unroll
@@ -325,10 +328,8 @@ __global__ __launch_bounds__(320, 1) void head_kernel(Plan p, int units, int gro
 #pragma unroll
       for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
-        for (int tt = 0; tt < 8; ++tt) {
-          const size_t off = (size_t)(16 * (vt0 + nt) + l16) * kHead + 16 * tt + 4 * g4;
-          store_state4<SDT>(out_plane, off, S[nt][tt]);
-        }
+        for (int tt = 0; tt < 8; ++tt)
+          store_state4_vk<SDT>(out_plane, 16 * (vt0 + nt) + l16, 16 * tt + 4 * g4, S[nt][tt], KF);
     }
   } else {
     // Map slot layout (kMapBytes): A as bf16 hi and lo planes, then C in fp32, each in
@@ -363,10 +364,10 @@ __global__ __launch_bounds__(320, 1) void head_kernel(Plan p, int units, int gro
 
 // One state row group of four: the segment's start state (fp32, from the combine
 // kernel), the call's initial state, or zero.
-template <int SDT>
-__device__ __forceinline__ f32x4 load_start4(const Plan& p, const Unit& u, const void* in_plane, size_t off) {
-  if (u.m_prev >= 0) return load_state4<kF32>(p.starts + ((size_t)u.m_prev * p.H + u.h) * kHead * kHead, off);
-  return in_plane ? load_state4<SDT>(in_plane, off) : zero4();
+template <int SDT, bool KF>
+__device__ __forceinline__ f32x4 load_start4(const Plan& p, const Unit& u, const void* in_plane, int v, int k) {
+  if (u.m_prev >= 0) return load_state4<kF32>(p.starts + ((size_t)u.m_prev * p.H + u.h) * kHead * kHead, (size_t)v * kHead + k);
+  return in_plane ? load_state4_vk<SDT>(in_plane, v, k, KF) : zero4();
 }
 
 // Output-tile fragments one output wave consumes per chunk (row tile t).
@@ -431,7 +432,7 @@ struct NarrowLds {
   __device__ static int db(int par, int nt) { return kRing + par * kPerParity + (4 * NT + nt) * 1024; }
 };
 
-template <int NT, int SDT, int RING, int DOUT>
+template <int NT, int SDT, int RING, int DOUT, bool KF>
 __global__ __launch_bounds__(256, 1) void scan_narrow(Plan p, int units, int groups) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   typedef NarrowLds<NT, RING> L;
@@ -505,10 +506,7 @@ __global__ __launch_bounds__(256, 1) void scan_narrow(Plan p, int units, int gro
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-      for (int tt = 0; tt < 8; ++tt) {
-        const size_t off = (size_t)(16 * (vtile0 + nt) + l16) * kHead + 16 * tt + 4 * g4;
-        S[nt][tt] = load_start4<SDT>(p, un, in_plane, off);
-      }
+      for (int tt = 0; tt < 8; ++tt) S[nt][tt] = load_start4<SDT, KF>(p, un, in_plane, 16 * (vtile0 + nt) + l16, 16 * tt + 4 * g4);
 
     // One chunk's fragments, read from its ring slot.
     // Issued together, in order of first use and pinned in that order (the scheduler
@@ -608,10 +606,8 @@ __global__ __launch_bounds__(256, 1) void scan_narrow(Plan p, int units, int gro
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-        for (int tt = 0; tt < 8; ++tt) {
-          const size_t off = (size_t)(16 * (vtile0 + nt) + l16) * kHead + 16 * tt + 4 * g4;
-          store_state4<SDT>(out_plane, off, S[nt][tt]);
-        }
+        for (int tt = 0; tt < 8; ++tt)
+          store_state4_vk<SDT>(out_plane, 16 * (vtile0 + nt) + l16, 16 * tt + 4 * g4, S[nt][tt], KF);
     }
   } else {
     // ------------------------------------------------------------ output waves
@@ -660,43 +656,48 @@ int set_lds_limit(KernelT* kernel, size_t bytes, bool& done) {
   return 0;
 }
 
-template <int NTW, int SDT>
+template <int NTW, int SDT, bool KF>
 int launch_scan_ntw(const Plan& p, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   constexpr size_t bytes = HeadLds<NTW>::kBytes;
   static_assert(bytes <= 160 * 1024, "fits one CU's LDS");
   static bool done = false;
-  if (int e = set_lds_limit(&head_kernel<NTW, SDT, kKernelScan>, bytes, done)) return e;
+  if (int e = set_lds_limit(&head_kernel<NTW, SDT, kKernelScan, KF>, bytes, done)) return e;
   const int groups = 2 / NTW;  // value-channel halves per (segment, head)
   const int units = p.n_seg * p.H;
   const int nblocks = 8 * ((units + 7) / 8) * groups;
-  hipExtLaunchKernelGGL((head_kernel<NTW, SDT, kKernelScan>), dim3(nblocks), dim3(320), bytes, s, e0, e1, 0, p, units,
+  hipExtLaunchKernelGGL((head_kernel<NTW, SDT, kKernelScan, KF>), dim3(nblocks), dim3(320), bytes, s, e0, e1, 0, p, units,
                         groups);
   return (int)hipGetLastError();
 }
 
-template <int NT, int SDT>
+template <int NT, int SDT, bool KF>
 int launch_narrow(const Plan& p, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   constexpr int R = 5;                 // ring slots: the loader runs 4 chunks ahead
   constexpr int DO = NT == 1 ? 4 : 3;  // output-wave fragment depth
   constexpr size_t bytes = NarrowLds<NT, R>::kBytes;
   static_assert(bytes <= 160 * 1024, "fits one CU's LDS");
   static bool done = false;
-  if (int e = set_lds_limit(&scan_narrow<NT, SDT, R, DO>, bytes, done)) return e;
+  if (int e = set_lds_limit(&scan_narrow<NT, SDT, R, DO, KF>, bytes, done)) return e;
   const int groups = 8 / NT;
   const int units = p.n_seg * p.H;
   const int nblocks = 8 * ((units + 7) / 8) * groups;
-  hipExtLaunchKernelGGL((scan_narrow<NT, SDT, R, DO>), dim3(nblocks), dim3(256), bytes, s, e0, e1, 0, p, units, groups);
+  hipExtLaunchKernelGGL((scan_narrow<NT, SDT, R, DO, KF>), dim3(nblocks), dim3(256), bytes, s, e0, e1, 0, p, units, groups);
   return (int)hipGetLastError();
+}
+
+template <int SDT, bool KF>
+int launch_scan_kf(const Plan& p, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  switch (p.dv_split) {
+    case 8: return launch_narrow<1, SDT, KF>(p, s, e0, e1);
+    case 4: return launch_narrow<2, SDT, KF>(p, s, e0, e1);
+    case 2: return launch_scan_ntw<1, SDT, KF>(p, s, e0, e1);
+    default: return launch_scan_ntw<2, SDT, KF>(p, s, e0, e1);
+  }
 }
 
 template <int SDT>
 int launch_scan_dt(const Plan& p, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
-  switch (p.dv_split) {
-    case 8: return launch_narrow<1, SDT>(p, s, e0, e1);
-    case 4: return launch_narrow<2, SDT>(p, s, e0, e1);
-    case 2: return launch_scan_ntw<1, SDT>(p, s, e0, e1);
-    default: return launch_scan_ntw<2, SDT>(p, s, e0, e1);
-  }
+  return p.kfirst ? launch_scan_kf<SDT, true>(p, s, e0, e1) : launch_scan_kf<SDT, false>(p, s, e0, e1);
 }
 
 }  // namespace
@@ -717,10 +718,10 @@ int launch_segmap(const Plan& p, void* stream, void* start, void* stop) {
   hipEvent_t e0 = reinterpret_cast<hipEvent_t>(start), e1 = reinterpret_cast<hipEvent_t>(stop);
   constexpr size_t bytes = HeadLds<2>::kBytes;
   static bool done = false;
-  if (int e = set_lds_limit(&head_kernel<2, kF32, kKernelMap>, bytes, done)) return e;
+  if (int e = set_lds_limit(&head_kernel<2, kF32, kKernelMap, false>, bytes, done)) return e;
   const int units = p.n_maps * p.H;
   const int nblocks = 8 * ((units + 7) / 8) * 2;  // halves A and C
-  hipExtLaunchKernelGGL((head_kernel<2, kF32, kKernelMap>), dim3(nblocks), dim3(320), bytes, s, e0, e1, 0, p, units, 2);
+  hipExtLaunchKernelGGL((head_kernel<2, kF32, kKernelMap, false>), dim3(nblocks), dim3(320), bytes, s, e0, e1, 0, p, units, 2);
   return (int)hipGetLastError();
 }
 

@@ -46,7 +46,7 @@ __global__ __launch_bounds__(256) void segcombine_kernel(Plan p) {
   const void* in_plane = state_in_plane<SDT>(p, n, h);
   for (int q = threadIdx.x; q < 32 * 32; q += 256) {
     const int r = q >> 5, c4 = (q & 31) * 4;
-    const f32x4 x = in_plane ? load_state4<SDT>(in_plane, (size_t)(32 * slice + r) * kHead + c4) : zero4();
+    const f32x4 x = in_plane ? load_state4_vk<SDT>(in_plane, 32 * slice + r, c4, p.kfirst) : zero4();
 #pragma unroll
     for (int i = 0; i < 4; ++i) split_bf16(x[i], Shi[r * kLdS + c4 + i], Slo[r * kLdS + c4 + i]);
   }

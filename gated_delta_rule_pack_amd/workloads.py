@@ -32,8 +32,8 @@ class Workload:
     """One synthetic KDA prefill call, all tensors on the CPU."""
 
     name: str
-    q: torch.Tensor  # [1, T, H, K] bf16
-    k: torch.Tensor  # [1, T, H, K] bf16
+    q: torch.Tensor  # [1, T, H_qk, K] bf16 (H_qk = H unless value heads are grouped)
+    k: torch.Tensor  # [1, T, H_qk, K] bf16
     v: torch.Tensor  # [1, T, H, V] bf16
     g_raw: torch.Tensor  # [1, T, H, K] fp32 (or bf16)
     beta_raw: torch.Tensor  # [1, T, H] fp32 (or bf16)
@@ -49,6 +49,7 @@ class Workload:
     num_slots: int = 0
     state_indices: Optional[torch.Tensor] = None  # [N] int32
     has_initial_state: Optional[torch.Tensor] = None  # [N] bool
+    state_k_first: bool = False  # stored state planes are [K, V] rather than [V, K]
     info: dict = field(default_factory=dict)
 
     @property
@@ -57,6 +58,12 @@ class Workload:
 
     @property
     def H(self) -> int:
+        """Value heads (v, gate, beta, out and state)."""
+        return int(self.v.shape[2])
+
+    @property
+    def H_qk(self) -> int:
+        """q/k heads; each serves H / H_qk consecutive value heads."""
         return int(self.q.shape[2])
 
     @property
@@ -107,12 +114,16 @@ def make_workload(
     poison: bool = True,
     want_final_state: bool = True,
     lengths_from_seed: Optional[tuple] = None,
+    H_qk: Optional[int] = None,
+    state_k_first: bool = False,
 ) -> Workload:
     """Draw one workload.
 
     ``lengths`` is a list of per-sequence token counts, or None when
     ``lengths_from_seed=(N, lo, hi, n_zero)`` asks for N lengths uniform in [lo, hi]
-    with ``n_zero`` positions (a seeded permutation) forced to 0.
+    with ``n_zero`` positions (a seeded permutation) forced to 0. ``H_qk`` (dividing
+    H) draws q and k with fewer heads than v; ``state_k_first`` marks the stored
+    planes as ``[K, V]`` (the random state draws are the same either way).
     """
     gen = torch.Generator("cpu").manual_seed(seed)
     if lengths is None:
@@ -128,8 +139,11 @@ def make_workload(
     N = len(lengths)
     K = V = HEAD_DIM
 
-    q = _randn(gen, (1, T, H, K)).to(torch.bfloat16)
-    k = _randn(gen, (1, T, H, K)).to(torch.bfloat16)
+    Hqk = H if H_qk is None else int(H_qk)
+    if Hqk < 1 or H % Hqk != 0:
+        raise ValueError(f"H_qk={Hqk} must divide H={H}")
+    q = _randn(gen, (1, T, Hqk, K)).to(torch.bfloat16)
+    k = _randn(gen, (1, T, Hqk, K)).to(torch.bfloat16)
     v = _randn(gen, (1, T, H, V)).to(torch.bfloat16)
     g_raw = (_randn(gen, (1, T, H, K)) + gate_shift).to(_DTYPES[gate_dtype])
     beta_raw = _randn(gen, (1, T, H)).to(_DTYPES[beta_dtype])
@@ -137,7 +151,7 @@ def make_workload(
     wl = Workload(
         name=name, q=q, k=k, v=v, g_raw=g_raw, beta_raw=beta_raw, cu_seqlens=cu,
         scale=1.0 / float(np.sqrt(K)), lower_bound=float(lower_bound), state_mode=state_mode,
-        state_dtype=state_dtype, info={"lengths": lengths, "seed": seed},
+        state_dtype=state_dtype, state_k_first=bool(state_k_first), info={"lengths": lengths, "seed": seed},
     )
     sdt = _DTYPES[state_dtype]
     if state_mode == "dense":

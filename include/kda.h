@@ -68,8 +68,8 @@ typedef struct kda_fwd_args {
   float scale;       /* read-out scale, finite; 1/sqrt(K) is the usual value */
   float lower_bound; /* gate lower bound, finite and <= 0 (the pages use -5) */
 
-  const void* q;        /* bf16 [T, H, K] */
-  const void* k;        /* bf16 [T, H, K] */
+  const void* q;        /* bf16 [T, H, K] ([T, H_qk, K] with grouped value heads) */
+  const void* k;        /* bf16 [T, H, K] ([T, H_qk, K] with grouped value heads) */
   const void* v;        /* bf16 [T, H, V] */
   const void* g_raw;    /* [T, H, K], dtype g_dtype (KDA_F32 or KDA_BF16): raw gate */
   const void* beta_raw; /* [T, H], dtype beta_dtype (KDA_F32 or KDA_BF16): raw beta */
@@ -87,10 +87,12 @@ typedef struct kda_fwd_args {
    *   dense: initial_state and/or final_state set (state_cache null);
    *   paged: state_cache set (initial_state and final_state null). */
   kda_dtype state_dtype;     /* element type of whichever state tensors are given */
-  const void* initial_state; /* dense [N, H, V, K], nullable (null -> zero) */
-  void* final_state;         /* dense [N, H, V, K], nullable (null -> not written) */
+  const void* initial_state; /* dense [N, H, V, K] ([N, H, K, V] when state_k_first),
+                                nullable (null -> zero) */
+  void* final_state;         /* dense, laid out as initial_state, nullable (null -> not written) */
   void* state_cache;         /* paged pool: slot s plane at state_cache + s*stride0 elements,
-                                laid out [H, V, K]; read and written in place */
+                                laid out [H, V, K] ([H, K, V] when state_k_first); read and
+                                written in place */
   int64_t num_slots;          /* slots in the pool (>= 1 when paged) */
   int64_t state_cache_stride0; /* elements between consecutive slots, >= H*V*K */
   const int32_t* state_indices;      /* [N] device: slot of each sequence. Not validated on the
@@ -100,6 +102,17 @@ typedef struct kda_fwd_args {
                                         and its slot is not read */
 
   void* out; /* bf16 [T, H, V], required; must not overlap v */
+
+  /* Grouped value heads (GVA; the default pipeline's head layout, aiter PR 5754, Technical
+   * Details). 0 means H (one q/k head per value head). Otherwise 1 <= H_qk <= H and H_qk
+   * divides H: q and k are then bf16 [T, H_qk, K], and value head h reads q/k head
+   * h / (H / H_qk). v, g_raw, beta_raw, out and the state keep H heads. Anything else
+   * returns KDA_ERR_INVALID_ARG. */
+  int32_t H_qk;
+  /* State plane layout for the dense tensors and the pool alike (same passage): 0 =
+   * V-first [V, K] (element (v, k) at v * K + k), 1 = K-first [K, V] (element (v, k) at
+   * k * V + v). Any other value returns KDA_ERR_INVALID_ARG. */
+  int32_t state_k_first;
 } kda_fwd_args;
 
 /* Counters kept per context. */

@@ -54,7 +54,7 @@ def device_inputs(wl: Workload, device="cuda"):
 
 def run_gpu(wl: Workload, device="cuda", host_bounds=True, inputs=None, sync=True, **kw):
     d = inputs if inputs is not None else device_inputs(wl, device)
-    args = dict(scale=wl.scale, lower_bound=wl.lower_bound)
+    args = dict(scale=wl.scale, lower_bound=wl.lower_bound, state_k_first=wl.state_k_first)
     if host_bounds:
         args["cu_seqlens_cpu"] = wl.cu_seqlens
     if wl.state_mode == "dense":
@@ -75,10 +75,14 @@ def run_gpu(wl: Workload, device="cuda", host_bounds=True, inputs=None, sync=Tru
 
 
 def run_oracle(wl: Workload, seqs=None, heads=None):
-    """fp64 oracle on (optionally) a subset of sequences and heads."""
+    """fp64 oracle on (optionally) a subset of sequences and value heads.
+
+    For a subset of value heads, each one's q/k head (h // (H / H_qk)) is selected here,
+    so the oracle sees one q/k head per selected value head."""
     hs = slice(None) if heads is None else list(heads)
-    q = to_f64(wl.q[0])[:, hs]
-    k = to_f64(wl.k[0])[:, hs]
+    qk_hs = slice(None) if heads is None else [h // (wl.H // wl.H_qk) for h in heads]
+    q = to_f64(wl.q[0])[:, qk_hs]
+    k = to_f64(wl.k[0])[:, qk_hs]
     v = to_f64(wl.v[0])[:, hs]
     g = to_f64(wl.g_raw[0])[:, hs]
     b = to_f64(wl.beta_raw[0])[:, hs]
@@ -90,11 +94,13 @@ def run_oracle(wl: Workload, seqs=None, heads=None):
         kw["state_cache"] = to_f64(wl.cache_view())[:, hs]
         kw["state_indices"] = wl.state_indices.numpy()
         kw["has_initial_state"] = wl.has_initial_state.numpy()
-    return kda_forward(q, k, v, g, b, cu, scale=wl.scale, lower_bound=wl.lower_bound, seqs=seqs, **kw)
+    return kda_forward(q, k, v, g, b, cu, scale=wl.scale, lower_bound=wl.lower_bound, seqs=seqs,
+                       state_k_first=wl.state_k_first, **kw)
 
 
 def gpu_final_states(wl: Workload, run: GpuRun):
-    """Per-sequence final states written by the GPU, as fp64 [N][H, V, K]."""
+    """Per-sequence final states written by the GPU, as fp64 [N][H, V, K] (the stored
+    layout: [N][H, K, V] for K-first planes)."""
     if wl.state_mode == "dense":
         return run.final_state
     if wl.state_mode == "paged":

@@ -93,6 +93,15 @@ def test_validation_accepts_valid_args(lib):
         assert _check(lib, a) == _lib.KDA_OK
 
 
+@pytest.mark.parametrize("H_qk,k_first", [(0, 1), (1, 0), (2, 1), (1, 1)])
+def test_validation_accepts_grouped_heads_and_k_first(lib, H_qk, k_first):
+    bufs = FakeBufs()
+    a, _, _ = _valid_args(bufs, paged=True)
+    assert a.H == 2
+    a.H_qk, a.state_k_first = H_qk, k_first
+    assert _check(lib, a) == _lib.KDA_OK
+
+
 @pytest.mark.parametrize("mutate,code", [
     (lambda a, b: setattr(a, "N", 0), _lib.KDA_ERR_INVALID_ARG),
     (lambda a, b: setattr(a, "T", -1), _lib.KDA_ERR_INVALID_ARG),
@@ -114,6 +123,10 @@ def test_validation_accepts_valid_args(lib):
     (lambda a, b: setattr(a, "state_indices", None), _lib.KDA_ERR_INVALID_ARG),
     (lambda a, b: setattr(a, "has_initial_state", None), _lib.KDA_ERR_INVALID_ARG),
     (lambda a, b: setattr(a, "num_slots", 0), _lib.KDA_ERR_INVALID_ARG),
+    (lambda a, b: setattr(a, "H_qk", -1), _lib.KDA_ERR_INVALID_ARG),
+    (lambda a, b: setattr(a, "H_qk", 3), _lib.KDA_ERR_INVALID_ARG),   # more q/k heads than value heads
+    (lambda a, b: (setattr(a, "H", 6), setattr(a, "H_qk", 4)), _lib.KDA_ERR_INVALID_ARG),  # 4 does not divide 6
+    (lambda a, b: setattr(a, "state_k_first", 2), _lib.KDA_ERR_INVALID_ARG),
 ])
 def test_validation_errors(lib, mutate, code):
     bufs = FakeBufs()
