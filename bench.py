@@ -39,6 +39,8 @@ WORKLOADS = {
     "paged_256x1_H12_bf16": "256 sequences x 1 token, H=12, paged bf16 pool [512,12,128,128]",
     "paged_64x1_H12_f16": "64 sequences x 1 token (one decode step), H=12, paged fp16 pool [128,12,128,128]",
     "paged_64x1_H12_f32": "64 sequences x 1 token (one decode step), H=12, paged fp32 pool [128,12,128,128]",
+    "paged_256x1_H12_bf16_kfirst": "256 sequences x 1 token, H=12, paged bf16 pool with K-first planes [512,12,128,128]",
+    "paged_1x4096_H12_qk6": "1x4096 tokens, 12 value heads sharing 6 q/k heads, paged fp32 pool [64,12,128,128]",
 }
 
 
@@ -72,13 +74,14 @@ def cpu_baseline(wl, max_tokens: int, workers: int, min_seconds: float):
     g = to_f64(wl.g_raw[0, :t_end]); b = to_f64(wl.beta_raw[0, :t_end])
     tasks = []
     for h in range(wl.H):
-        S = {}
+        hq = h // (wl.H // wl.H_qk)  # the q/k head this value head reads
+        S = {"state_k_first": wl.state_k_first}
         if wl.state_mode == "paged":
             S = dict(state_cache=to_f64(wl.cache_view()[:, h:h + 1]), state_indices=wl.state_indices.numpy()[:take],
                      has_initial_state=wl.has_initial_state.numpy()[:take])
         elif wl.state_mode == "dense":
             S = dict(initial_state=to_f64(wl.initial_state[:take, h:h + 1]))
-        tasks.append((q[:, h:h + 1], k[:, h:h + 1], v[:, h:h + 1], g[:, h:h + 1], b[:, h:h + 1], cu_s,
+        tasks.append((q[:, hq:hq + 1], k[:, hq:hq + 1], v[:, h:h + 1], g[:, h:h + 1], b[:, h:h + 1], cu_s,
                       wl.scale, wl.lower_bound, S))
     workers = max(1, min(workers, len(tasks)))
     with threadpool_limits(1):
@@ -328,7 +331,8 @@ def main():
         s = inputs[i % n_rot]
         b_d, b_h = bounds[i % len(bounds)]
         a = kda.make_args(s["q"], s["k"], s["v"], s["g_raw"], s["beta_raw"], b_d, cu_seqlens_cpu=b_h,
-                          scale=wl.scale, lower_bound=wl.lower_bound, out=s["out"], **pools[i % len(pools)])
+                          scale=wl.scale, lower_bound=wl.lower_bound, out=s["out"], state_k_first=wl.state_k_first,
+                          **pools[i % len(pools)])
         rc = lib.kda_chunk_fwd_validate(ctypes.byref(a))
         if rc != _lib.KDA_OK:
             raise kda.KDAError(rc, "validate")
@@ -403,7 +407,8 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
         "us_per_call": round(ms_step * 1e3, 2), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": args.workload, "description": cfg_desc, "T": wl.T, "N": wl.N, "H": wl.H, "K": 128, "V": 128, "chunk": 32,
+        "config": {"workload": args.workload, "description": cfg_desc, "T": wl.T, "N": wl.N, "H": wl.H,
+                   "H_qk": wl.H_qk, "K": 128, "V": 128, "chunk": 32, "state_k_first": wl.state_k_first,
                    "lower_bound": wl.lower_bound, "state": f"{wl.state_mode} {wl.state_dtype}",
                    "dv_split": stats["last_dv_split"], "ref_block": stats["last_ref_block"],
                    "input_sets_rotated": n_rot, "bounds_sets": max(1, args.rotate_bounds),

@@ -360,7 +360,11 @@ kda_status get_meta(kda_ctx* ctx, const int32_t* cu, int N, int seg_len, void* s
   for (CacheEntry* e : ctx->cache) {
     if (e->hash == hsh && e->seg_len == seg_len && (int)e->bounds.size() == N + 1 &&
         std::memcmp(e->bounds.data(), cu, (N + 1) * sizeof(int32_t)) == 0) {
-      if (e->upload_stream != stream && e->upload_event) {
+      // A hit from another stream waits for the upload. Under capture the wait would
+      // join an event recorded outside the graph, which capture does not allow: the
+      // caller guarantees instead that the call that filled the entry has completed
+      // before the graph is launched.
+      if (!capturing && e->upload_stream != stream && e->upload_event) {
         if (ctx->rt.stream_wait_event(ctx->rt.user, stream, e->upload_event)) return hip_fail();
       }
       if (capturing) e->retained = true;

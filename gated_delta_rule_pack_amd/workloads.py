@@ -204,6 +204,11 @@ STANDARD = {
                                state_dtype="f16", num_slots=128),
     "paged_64x1_H12_f32": dict(lengths=[1] * 64, H=12, seed=1007, state_mode="paged",
                                state_dtype="f32", num_slots=128),
+    # The same shapes with K-first state planes, and with grouped value heads (6 q/k heads
+    # for 12 value heads).
+    "paged_256x1_H12_bf16_kfirst": dict(lengths=[1] * 256, H=12, seed=1005, state_mode="paged",
+                                        state_dtype="bf16", num_slots=512, state_k_first=True),
+    "paged_1x4096_H12_qk6": dict(lengths=[4096], H=12, H_qk=6, seed=1002, state_mode="paged", num_slots=64),
 }
 
 

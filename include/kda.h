@@ -191,9 +191,19 @@ kda_status kda_chunk_fwd_validate(const kda_fwd_args* args);
 /* Forward call. Validates, resolves metadata (cache hit, or one asynchronous upload from
  * pinned memory), then enqueues prep, the segment kernels when the call is segmented,
  * and scan on stream (a hipStream_t; null = default
- * stream) and returns without waiting. The workspace (caller-owned device memory of at
- * least kda_chunk_fwd_workspace_bytes(args) bytes, 256-byte aligned) must stay
- * allocated and unused by anything else until the stream work completes. */
+ * stream) and returns without waiting. When no sequence of the call has more than one
+ * token, a single fused decode kernel replaces prep and scan (aiter PR 4741,
+ * Performance: decode runs a fused update, not the chunked path). The workspace
+ * (caller-owned device memory of at least kda_chunk_fwd_workspace_bytes(args) bytes,
+ * 256-byte aligned) must stay allocated and unused by anything else until the stream
+ * work completes.
+ *
+ * Graph capture (aiter PR 6912, Changes): while stream is being captured the call needs
+ * its metadata already cached. A miss, or a call without cu_seqlens_host (whose
+ * read-back cannot be captured), returns KDA_ERR_CAPTURE_MISS and enqueues nothing. A hit
+ * marks the cached entry as retained: it is never evicted, so the graph can be launched
+ * for as long as the context lives. Captured launches carry no events. The call that
+ * filled the cache entry must have completed before the graph is first launched. */
 kda_status kda_chunk_fwd(kda_ctx* ctx, const kda_fwd_args* args, void* workspace,
                          size_t workspace_bytes, void* stream);
 

@@ -527,10 +527,12 @@ def test_capture_miss_is_an_error_and_hit_is_retained(lib, fake):
     fake.capturing.add(0x20)
     assert _call(lib, fake, a, stream=0x20) == _lib.KDA_ERR_CAPTURE_MISS
     assert fake.launches == []
-    # Populate the cache outside capture, then hit it under capture.
+    # Populate the cache outside capture, then hit it under capture. The hit comes from
+    # another stream but joins no event recorded outside the capture.
     assert _call(lib, fake, a, stream=0x10) == _lib.KDA_OK
     fake.complete_all()
     assert _call(lib, fake, a, stream=0x20) == _lib.KDA_OK
+    assert [e for e in fake.log if e[0] == "wait"] == []
     # Retained: flood the cache with other bounds; the captured entry must survive.
     for i in range(80):
         b, _, _ = _valid_args(bufs, T=100 + i, N=1, cu=np.array([0, 100 + i], np.int32))

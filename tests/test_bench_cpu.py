@@ -45,3 +45,13 @@ def test_more_than_one_gpu_is_refused(gpus):
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout == ""
+
+
+def test_grouped_heads_read_fewer_qk_bytes():
+    # 12 value heads share 6 q/k heads: q and k move 256 B per token-head instead of 512.
+    g = standard("paged_1x4096_H12_qk6")
+    f = standard("paged_1x4096_H12")
+    assert g.H == f.H == 12 and g.H_qk == 6
+    th = 4096 * 12
+    assert bench.algorithmic_bytes(f, "call", 128) - bench.algorithmic_bytes(g, "call", 128) == th * 256
+    assert bench.algorithmic_bytes(f, "scan", 128) == bench.algorithmic_bytes(g, "scan", 128)
