@@ -214,8 +214,9 @@ int32_t dv_split_for(int32_t units_n, int32_t H, int32_t cus) {
 }
 
 // Segment length of the segmented scan: only few, long sequences are split (many
-// (sequence, head) units already fill the chip, and below 32 chunks the serial walk is
-// short); about 16 segments for the longest sequence, at least kSegMin chunks each.
+// (sequence, head) units already fill the chip, and below 256 chunks the maps and their
+// combination cost more than the shorter walk saves); about 8 segments for the longest
+// sequence, at least kSegMin chunks each.
 int32_t seg_len_for(int32_t N, int32_t H, int64_t max_chunks) {
   if ((int64_t)N * H > 96 || max_chunks < 256) return 0;
   return (int32_t)std::max<int64_t>(kda::kSegMin, (max_chunks + 7) / 8);
