@@ -323,14 +323,153 @@ __global__ __launch_bounds__(256) void decode_kfirst_kernel(Plan p) {
   }
 }
 
+// K-first planes with a 2-byte state. A 128-byte line holds 64 columns of one key row, so
+// eight lanes cover a line and every load reads eight whole rows. Wave w owns columns
+// 64 (w & 1) .. +63 and key rows 64 (w >> 1) .. +63; lane (vo = lane & 7, ko = lane >> 3)
+// holds the eight columns 64 (w & 1) + 8 vo .. +7 of rows 64 (w >> 1) + 8 i + ko
+// (i = 0..7). The sums over k (u and o) run over the lane's eight rows, then over the
+// eight lanes of its column group, then over the two waves of its column half (LDS).
+template <int SDT, bool GF32>
+__global__ __launch_bounds__(256) void decode_kfirst2_kernel(Plan p) {
+  static_assert(SDT != kF32, "2-byte states only");
+  __shared__ float part[2][2][kHead];  // [u, o][key half][column]
+  const int n = blockIdx.x / p.H;
+  const int h = blockIdx.x - n * p.H;
+  const int hqk = __builtin_amdgcn_readfirstlane(h / p.group);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int vo = lane & 7, ko = lane >> 3;
+  const int half = wave >> 1;                        // key half of this wave
+  const int c0 = 64 * (wave & 1) + 8 * vo;           // first of the lane's columns
+  const int r0 = 64 * half + ko;                     // the lane's rows are r0 + 8 i
+  const int t0 = __builtin_amdgcn_readfirstlane(p.d_cu[n]);
+  const bool has_token = __builtin_amdgcn_readfirstlane(p.d_cu[n + 1]) > t0;
+
+  const void* in_plane = state_in_plane<SDT>(p, n, h);
+  Row8<SDT> raw[kIters];
+#pragma unroll
+  for (int i = 0; i < kIters; ++i) {
+    if (in_plane) raw[i] = load_row8<SDT>(in_plane, (size_t)(r0 + 8 * i) * kHead + c0);
+    else raw[i] = Row8<SDT>{};
+  }
+  void* out_plane = state_out_plane<SDT>(p, n, h);
+
+  if (has_token) {  // the same for the whole workgroup: its barriers are reached by all
+    const size_t tok = ((size_t)t0 * p.H + h) * kHead;
+    const size_t tqk = ((size_t)t0 * p.H_qk + hqk) * kHead;
+    const uint16_t* q16 = reinterpret_cast<const uint16_t*>(p.q) + tqk;
+    const uint16_t* k16 = reinterpret_cast<const uint16_t*>(p.k) + tqk;
+    // Norms over all 128 keys: two keys per lane, summed over the wave.
+    const uint32_t qw = *reinterpret_cast<const uint32_t*>(q16 + 2 * lane);
+    const uint32_t kw = *reinterpret_cast<const uint32_t*>(k16 + 2 * lane);
+    float sq = bf16_bits_to_f32(qw & 0xffffu) * bf16_bits_to_f32(qw & 0xffffu) +
+               bf16_bits_to_f32(qw >> 16) * bf16_bits_to_f32(qw >> 16);
+    float sk = bf16_bits_to_f32(kw & 0xffffu) * bf16_bits_to_f32(kw & 0xffffu) +
+               bf16_bits_to_f32(kw >> 16) * bf16_bits_to_f32(kw >> 16);
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+      sq += __shfl_xor(sq, m);
+      sk += __shfl_xor(sk, m);
+    }
+    const float rq = rsqrtf(sq + 1e-6f) * p.scale;  // scale folded into q-hat
+    const float rk = rsqrtf(sk + 1e-6f);
+    float qh[kIters], kh[kIters], eg[kIters];
+#pragma unroll
+    for (int i = 0; i < kIters; ++i) {
+      const int r = r0 + 8 * i;
+      qh[i] = bf16_bits_to_f32(q16[r]) * rq;
+      kh[i] = bf16_bits_to_f32(k16[r]) * rk;
+      const float gr = GF32 ? reinterpret_cast<const float*>(p.g_raw)[tok + r]
+                            : bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(p.g_raw)[tok + r]);
+      eg[i] = __expf(p.lower_bound * sigmoid(gr));
+    }
+    const size_t bidx = (size_t)t0 * p.H + h;
+    const float braw = p.beta_dtype == kF32 ? reinterpret_cast<const float*>(p.beta_raw)[bidx]
+                                            : bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(p.beta_raw)[bidx]);
+    const float beta = sigmoid(braw);
+    const uint4 vw = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(p.v) + tok + c0);
+    const uint32_t v32[4] = {vw.x, vw.y, vw.z, vw.w};
+
+    // u = D k-hat for the lane's columns: own rows, the column group, the two key halves.
+    float pu[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < kIters; ++i) {
+      const float w = eg[i] * kh[i];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) pu[j] += row8_get<SDT>(raw[i], j) * w;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      pu[j] += __shfl_xor(pu[j], 8);
+      pu[j] += __shfl_xor(pu[j], 16);
+      pu[j] += __shfl_xor(pu[j], 32);
+    }
+    if (ko == 0)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) part[0][half][c0 + j] = pu[j];
+    __syncthreads();
+    float c[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float vj = __uint_as_float((j & 1) ? (v32[j >> 1] & 0xffff0000u) : (v32[j >> 1] << 16));
+      c[j] = beta * (vj - (part[0][0][c0 + j] + part[0][1][c0 + j]));
+    }
+    // Update, store each key row as soon as it is done, and accumulate o = S q-hat.
+    float po[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < kIters; ++i) {
+      float x[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        x[j] = row8_get<SDT>(raw[i], j) * eg[i] + c[j] * kh[i];
+        po[j] += x[j] * qh[i];
+      }
+      if (out_plane) store_row8<SDT>(out_plane, (size_t)(r0 + 8 * i) * kHead + c0, x);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      po[j] += __shfl_xor(po[j], 8);
+      po[j] += __shfl_xor(po[j], 16);
+      po[j] += __shfl_xor(po[j], 32);
+    }
+    if (ko == 0)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) part[1][half][c0 + j] = po[j];
+    __syncthreads();
+    if (half == 0 && ko == 0) {
+      uint32_t w[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float a = part[1][0][c0 + 2 * j] + part[1][1][c0 + 2 * j];
+        const float b = part[1][0][c0 + 2 * j + 1] + part[1][1][c0 + 2 * j + 1];
+        w[j] = (uint32_t)__builtin_bit_cast(uint16_t, to_bf16(a)) |
+               ((uint32_t)__builtin_bit_cast(uint16_t, to_bf16(b)) << 16);
+      }
+      *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(p.out) + tok + c0) = uint4{w[0], w[1], w[2], w[3]};
+    }
+  } else if (out_plane) {
+    // No token: the state is written back as read (zero when nothing was read).
+#pragma unroll
+    for (int i = 0; i < kIters; ++i)
+      *reinterpret_cast<uint4*>(reinterpret_cast<char*>(out_plane) +
+                                ((size_t)(r0 + 8 * i) * kHead + c0) * elem_size<SDT>()) = raw[i].w[0];
+  }
+}
+
 template <int SDT>
 int launch_sdt(const Plan& p, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   const dim3 grid(p.N * p.H);
   if (p.kfirst) {
-    if (p.g_dtype == kF32)
-      hipExtLaunchKernelGGL((decode_kfirst_kernel<SDT, true>), grid, dim3(256), 0, s, e0, e1, 0, p);
-    else
-      hipExtLaunchKernelGGL((decode_kfirst_kernel<SDT, false>), grid, dim3(256), 0, s, e0, e1, 0, p);
+    if constexpr (SDT == kF32) {  // four lanes already cover a line
+      if (p.g_dtype == kF32)
+        hipExtLaunchKernelGGL((decode_kfirst_kernel<SDT, true>), grid, dim3(256), 0, s, e0, e1, 0, p);
+      else
+        hipExtLaunchKernelGGL((decode_kfirst_kernel<SDT, false>), grid, dim3(256), 0, s, e0, e1, 0, p);
+    } else if (p.g_dtype == kF32) {
+      hipExtLaunchKernelGGL((decode_kfirst2_kernel<SDT, true>), grid, dim3(256), 0, s, e0, e1, 0, p);
+    } else {
+      hipExtLaunchKernelGGL((decode_kfirst2_kernel<SDT, false>), grid, dim3(256), 0, s, e0, e1, 0, p);
+    }
   } else if (p.g_dtype == kF32) {
     hipExtLaunchKernelGGL((decode_kernel<SDT, true>), grid, dim3(256), 0, s, e0, e1, 0, p);
   } else {
