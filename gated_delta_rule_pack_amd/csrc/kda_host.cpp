@@ -222,6 +222,12 @@ int32_t seg_len_for(int32_t N, int32_t H, int64_t max_chunks) {
   return (int32_t)std::max<int64_t>(kda::kSegMin, (max_chunks + 7) / 8);
 }
 
+// The scan addresses one segment's chunk records through a buffer descriptor with a
+// 32-bit size: a segment may span at most INT32_MAX bytes of records (60 786 chunks).
+// Segmentation keeps every sequence of a call with N * H <= 96 far below that unless
+// H = 1 and a sequence has more than about 15.5 M tokens.
+bool walk_fits(int64_t seg_chunks) { return seg_chunks * (int64_t)kda::kRecBytes <= (int64_t)INT32_MAX; }
+
 int32_t ref_block_for(float lb) {
   const float a = std::fabs(lb);
   for (int s : {16, 8, 4, 2})
@@ -502,7 +508,12 @@ kda_status kda_chunk_fwd_validate(const kda_fwd_args* a) {
     const size_t tok_bytes = (size_t)a->T * a->H * kHead * 2;
     if (ranges_overlap(a->out, tok_bytes, a->v, tok_bytes)) return KDA_ERR_ALIAS;
   }
-  if (a->cu_seqlens_host && !bounds_ok(a->cu_seqlens_host, a->N, a->T)) return KDA_ERR_INVALID_ARG;
+  if (a->cu_seqlens_host) {
+    if (!bounds_ok(a->cu_seqlens_host, a->N, a->T)) return KDA_ERR_INVALID_ARG;
+    const int64_t mc = max_seq_chunks(a->cu_seqlens_host, a->N);
+    const int32_t L = seg_len_for(a->N, a->H, mc);
+    if (!walk_fits(L > 0 ? L : mc)) return KDA_ERR_UNSUPPORTED;
+  }
   return KDA_OK;
 }
 
@@ -665,6 +676,7 @@ kda_status kda_chunk_fwd(kda_ctx* ctx, const kda_fwd_args* a, void* ws, size_t w
   const bool decode = max_seq_len(cu, a->N) <= 1 && !ctx->decode_off;
   int seg_len = seg_len_for(a->N, a->H, max_seq_chunks(cu, a->N));
   if (ctx->seg_len_override >= 0 && (int64_t)a->N * a->H <= 96) seg_len = ctx->seg_len_override;
+  if (!decode && !walk_fits(seg_len > 0 ? seg_len : max_seq_chunks(cu, a->N))) return KDA_ERR_UNSUPPORTED;
   CacheEntry* e = nullptr;
   int capturing = 0;
   st = get_meta(ctx, cu, a->N, seg_len, stream, &e, capturing);

@@ -46,7 +46,10 @@ extern "C" {
 typedef enum kda_status {
   KDA_OK = 0,
   KDA_ERR_INVALID_ARG = 1,  /* null required pointer, N < 1, T < 0, bad bounds, non-finite scale */
-  KDA_ERR_UNSUPPORTED = 2,  /* K or V != 128, dtype not allowed, lower_bound > 0, not gfx950 */
+  KDA_ERR_UNSUPPORTED = 2,  /* K or V != 128, dtype not allowed, lower_bound > 0, not gfx950,
+                               T * H > 2^31 / 128, or a scan walk over more than 2^31 bytes of
+                               chunk records (over 60 786 chunks in one segment: only with
+                               H = 1 and a sequence of more than about 15.5 M tokens) */
   KDA_ERR_STATE_MODE = 3,   /* dense and paged state both given, or final_state with a pool */
   KDA_ERR_STRIDE = 4,       /* state_cache_stride0 < H*V*K */
   KDA_ERR_ALIAS = 5,        /* the byte ranges of out and v overlap */

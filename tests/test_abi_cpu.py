@@ -601,3 +601,22 @@ def test_profiling_hook_reads_and_clears(lib, fake):
     assert n.value == 3 and p.value == 3.0 and s.value == 3.0
     assert lib.kda_profile_read(fake.ctx, ctypes.byref(p), ctypes.byref(s), ctypes.byref(n)) == _lib.KDA_OK
     assert n.value == 0
+
+
+def test_validation_rejects_record_walk_beyond_32_bits(lib):
+    """One head and one very long sequence: the segmented scan walk of 62 500 chunks would
+    span more than 2^31 bytes of records (rejected); 58 594 chunks fit. Validation touches
+    no device memory, so the device pointers here are placeholders."""
+    a = _lib.FwdArgs()
+    a.N, a.H, a.K, a.V = 1, 1, 128, 128
+    a.scale, a.lower_bound = 0.088, -5.0
+    base = 1 << 44
+    for i, name in enumerate(("q", "k", "v", "g_raw", "beta_raw", "out", "cu_seqlens")):
+        setattr(a, name, base + (i << 36))  # 16-byte aligned, 64 GiB apart: no overlap
+    a.g_dtype = a.beta_dtype = a.state_dtype = _lib.KDA_F32
+    for T, want in ((16_000_000, _lib.KDA_ERR_UNSUPPORTED), (15_000_000, _lib.KDA_OK)):
+        cu = np.array([0, T], np.int32)
+        a.T = T
+        a.cu_seqlens_host = cu.ctypes.data
+        assert lib.kda_seg_len(1, 1, -(-T // 32)) > 0
+        assert lib.kda_chunk_fwd_validate(ctypes.byref(a)) == want, T
