@@ -158,6 +158,33 @@ void build_meta(const int32_t* cu, const Meta& m, int32_t* buf) {
   int64_t c = 0;
   int s = 0, mbase = 0, k = 0;
   for (int i = 0; i <= m.N; ++i) buf[m.off_cu + i] = cu[i];
+  if (m.seg_len <= 0) {
+    // One segment per sequence, listed longest first: the scan deals its units in table
+    // order, so the longest walks start first and the short ones fill in behind them
+    // (which workgroup takes which sequence changes nothing in the results).
+    std::vector<int> order(m.N);
+    for (int i = 0; i < m.N; ++i) order[i] = i;
+    std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return cu[a + 1] - cu[a] > cu[b + 1] - cu[b]; });
+    for (int i = 0; i < m.N; ++i) {
+      co[i] = (int32_t)c;
+      const int nc = (cu[i + 1] - cu[i] + kChunk - 1) / kChunk;
+      for (int j = 0; j < nc; ++j, ++c) {
+        table[2 * c] = i;
+        table[2 * c + 1] = j;
+      }
+    }
+    for (int r = 0; r < m.N; ++r) {
+      const int i = order[r];
+      int32_t* e = seg + (size_t)kda::kSegInts * r;
+      e[0] = i;
+      e[1] = 0;
+      e[2] = (cu[i + 1] - cu[i] + kChunk - 1) / kChunk;
+      e[3] = -1;
+      e[4] = -1;
+    }
+    co[m.N] = (int32_t)c;
+    return;
+  }
   for (int i = 0; i < m.N; ++i) {
     co[i] = (int32_t)c;
     const int nc = (cu[i + 1] - cu[i] + kChunk - 1) / kChunk;

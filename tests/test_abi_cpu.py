@@ -510,6 +510,29 @@ def test_segmented_call_launches_and_tables(lib, fake):
         assert np.all(mine[1:, 1] == mine[:-1, 1] + mine[:-1, 2])
 
 
+def test_unsegmented_table_lists_longest_sequences_first(lib, fake):
+    """Without segmentation every sequence is one scan unit; the uploaded segment table
+    lists them longest first (ties in sequence order), each exactly once, with its whole
+    chunk count, no start-state slot and the final-state write."""
+    bufs = FakeBufs()
+    lens = [100, 0, 2048, 33, 2048, 1, 640, 0]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    N, T, H = len(lens), int(cu[-1]), 16   # N * H > 96: not segmented
+    a, _, _ = _valid_args(bufs, T=T, N=N, H=H, cu=cu, paged=True)
+    assert _call(lib, fake, a) == _lib.KDA_OK
+    assert _stats(lib, fake)["last_seg_len"] == 0
+    words = fake.uploads[0][3]
+    a4 = lambda n: (n + 3) // 4 * 4
+    n_chunks = int(sum(-(-x // 32) for x in lens))
+    off_seg = 2 * a4(N + 1) + a4(2 * n_chunks)
+    segs = np.asarray(words[off_seg:off_seg + 8 * N]).reshape(N, 8)
+    order = sorted(range(N), key=lambda n: -lens[n])
+    assert segs[:, 0].tolist() == order
+    assert segs[:, 2].tolist() == [-(-lens[n] // 32) for n in order]
+    assert np.all(segs[:, 1] == 0) and np.all(segs[:, 3] == -1) and np.all(segs[:, 4] == -1)
+    assert np.all(segs[:, 5:] == 0)
+
+
 def test_device_bounds_read_back_once(lib, fake):
     bufs = FakeBufs()
     a, _, _ = _valid_args(bufs, T=100, N=3)
