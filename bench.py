@@ -37,6 +37,7 @@ WORKLOADS = {
     "paged_1x16384_H12_pad": "1x16384 tokens, H=12, K=V=128, paged fp32 pool with stride(0) padded by 4096",
     "paged_varlen128_H12": "128 varlen sequences (0..2048 tokens, 4 empty), H=12, paged fp32 pool [256,...]",
     "paged_256x1_H12_bf16": "256 sequences x 1 token, H=12, paged bf16 pool [512,12,128,128]",
+    "paged_256x1_H12_f16": "256 sequences x 1 token, H=12, paged fp16 pool [512,12,128,128]",
     "paged_64x1_H12_f16": "64 sequences x 1 token (one decode step), H=12, paged fp16 pool [128,12,128,128]",
     "paged_64x1_H12_f32": "64 sequences x 1 token (one decode step), H=12, paged fp32 pool [128,12,128,128]",
     "paged_256x1_H12_bf16_kfirst": "256 sequences x 1 token, H=12, paged bf16 pool with K-first planes [512,12,128,128]",

@@ -199,6 +199,8 @@ STANDARD = {
                                 has_initial="bernoulli", lengths_from_seed=(128, 0, 2048, 4)),
     "paged_256x1_H12_bf16": dict(lengths=[1] * 256, H=12, seed=1005, state_mode="paged",
                                  state_dtype="bf16", num_slots=512),
+    "paged_256x1_H12_f16": dict(lengths=[1] * 256, H=12, seed=1005, state_mode="paged",
+                                state_dtype="f16", num_slots=512),
     # One decode step of 64 sequences at the per-GPU head count, 2-byte and 4-byte state.
     "paged_64x1_H12_f16": dict(lengths=[1] * 64, H=12, seed=1006, state_mode="paged",
                                state_dtype="f16", num_slots=128),
