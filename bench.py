@@ -394,7 +394,9 @@ def main():
     roofline = {
         "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
         "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-        "kernel": f"kda_{dom}", "kernel_us": round(k_us[dom], 2), "algorithmic_bytes": int(ab),
+        "kernel": f"kda_{dom}" + (" phase: segment maps, segment combine, scan"
+                                   if dom == "scan" and stats["last_seg_len"] > 0 else ""),
+        "kernel_us": round(k_us[dom], 2), "algorithmic_bytes": int(ab),
         "call_algorithmic_bytes": int(call_bytes),
         "call_frac": round(call_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "kernel_tflops": round(flops / (k_us[dom] * 1e-6) / 1e12, 2),
