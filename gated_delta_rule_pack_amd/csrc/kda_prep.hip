@@ -224,7 +224,13 @@ __device__ __forceinline__ int lane_of_sum(int v) {
 }
 
 template <int REF>
-__device__ void process_item(const Plan& p, const Item& it, const Inputs& in, char* lds, int w, int lane) {
+__device__ void process_item(const Plan& p, const Item& it, const Inputs& in, char* lds, int w_in, int lane) {
+  // The wave index is uniform, so everything derived from it (fragment and tile choices,
+  // LDS offsets, branch masks) is scalar. Redefining it here for the compiler keeps those
+  // values from being hoisted out of the item loop, where they would stay live across
+  // the whole kernel and spill scalar registers into vector lanes.
+  int w = w_in;
+  asm volatile("" : "+s"(w));
   constexpr int NB = 32 / REF;
   constexpr int OX = off_x(REF);
   float* tot = reinterpret_cast<float*>(lds + kOffTot);
