@@ -35,6 +35,8 @@ RECORD_BYTES = 35328  # per (head, chunk) workspace record written by prep, read
 WORKLOADS = {
     "paged_1x4096_H12": "1x4096 tokens, H=12, K=V=128, paged fp32 state pool [64,12,128,128]",
     "paged_1x16384_H12_pad": "1x16384 tokens, H=12, K=V=128, paged fp32 pool with stride(0) padded by 4096",
+    "paged_1x16384_H12_pad_lb20": "1x16384 tokens, H=12, steep gate (lower bound -20, raw gate +6: ~640 nats per chunk), "
+                                  "paged fp32 pool with stride(0) padded by 4096",
     "paged_varlen128_H12": "128 varlen sequences (0..2048 tokens, 4 empty), H=12, paged fp32 pool [256,...]",
     "paged_256x1_H12_bf16": "256 sequences x 1 token, H=12, paged bf16 pool [512,12,128,128]",
     "paged_256x1_H12_f16": "256 sequences x 1 token, H=12, paged fp16 pool [512,12,128,128]",

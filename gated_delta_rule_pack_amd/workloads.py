@@ -195,6 +195,10 @@ STANDARD = {
     "paged_1x4096_H12": dict(lengths=[4096], H=12, seed=1002, state_mode="paged", num_slots=64),
     "paged_1x16384_H12_pad": dict(lengths=[16384], H=12, seed=1003, state_mode="paged", num_slots=64,
                                   stride_pad=4096),
+    # The same call with a steep gate: lower bound -20 and the raw gate shifted by +6, about
+    # 640 nats of decay per chunk (prep then uses 4-row reference blocks).
+    "paged_1x16384_H12_pad_lb20": dict(lengths=[16384], H=12, seed=1003, state_mode="paged", num_slots=64,
+                                       stride_pad=4096, lower_bound=-20.0, gate_shift=6.0),
     "paged_varlen128_H12": dict(lengths=None, H=12, seed=1004, state_mode="paged", num_slots=256,
                                 has_initial="bernoulli", lengths_from_seed=(128, 0, 2048, 4)),
     "paged_256x1_H12_bf16": dict(lengths=[1] * 256, H=12, seed=1005, state_mode="paged",
