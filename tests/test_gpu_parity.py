@@ -66,9 +66,12 @@ def test_bf16_gate_and_beta_inputs():
     _say(f"  out {e_out:.3e} state {e_state:.3e}")
 
 
-@pytest.mark.parametrize("lb,shift", [(-5.0, 6.0), (-20.0, 6.0), (-1.0, -4.0), (0.0, 0.0), (-100.0, 0.0)])
+@pytest.mark.parametrize("lb,shift", [(-5.0, 6.0), (-8.0, 0.0), (-8.0, 6.0), (-20.0, 6.0), (-40.0, 0.0),
+                                      (-40.0, 6.0), (-1.0, -4.0), (0.0, 0.0), (-100.0, 0.0)])
 def test_gate_regimes_ref_blocks(lb, shift):
-    """Saturated gates (160 / 640 nats per chunk), weak decay, no decay, huge decay."""
+    """Saturated gates (160 / 640 nats per chunk), weak decay, no decay, huge decay; every
+    reference-row block the prep kernel has: 16 (lb -5, -1, 0), 8 (lb -8), 4 (lb -20),
+    2 (lb -40) and 1 (lb -100)."""
     wl = make_workload("gates", [100, 64], H=2, seed=15, state_mode="dense", lower_bound=lb, gate_shift=shift)
     run = run_gpu(wl)
     e_out, e_state = compare(wl, run)
