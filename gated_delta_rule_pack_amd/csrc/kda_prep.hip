@@ -321,7 +321,10 @@ __device__ void process_item(const Plan& p, const Item& it, const Inputs& in, ch
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int r = 8 * w + i;
-      const float2 gm = REF >= 8 ? gw : *reinterpret_cast<const float2*>(Gref + (r / REF) * 128 + c0);
+      // Below REF = 16 the rows of the lower half first take row 16 as their reference
+      // (the pivot of the off-diagonal tile, see below).
+      const int gi = REF == 16 ? 0 : (w >= 2 ? 16 / REF : r / REF);
+      const float2 gm = REF == 16 ? gw : *reinterpret_cast<const float2*>(Gref + gi * 128 + c0);
       const float e0 = ex2(G[i][0] - gm.x), e1 = ex2(G[i][1] - gm.y);  // in [e^-80, 1]
       uint32_t kh, kl, qh, ql;
       split2(kn[i][0] * e0, kn[i][1] * e1, kh, kl);
@@ -416,50 +419,97 @@ __device__ void process_item(const Plan& p, const Item& it, const Inputs& in, ch
       }
     }
     __syncthreads();
-  } else
-  for (int b = 0; b < NB; ++b) {
-    const int mb = b * REF;
-    const int lim = mb + REF - 1;  // last row of the block: right factors beyond it are 0
-    {
-      const float2 gm = *reinterpret_cast<const float2*>(Gref + b * 128 + c0);
+  } else {
+    // Below REF = 16 the two diagonal 16 x 16 tiles are built from REF-row sub-blocks and
+    // the off-diagonal tile (rows 16..31, columns 0..15) through row 16: for r >= 16 > i,
+    // e^{G_r - G_i} = e^{G_r - G_16} e^{G_16 - G_i}, both factors <= 1 whatever the decay.
+    // Jobs: wave 0 (0,0,A) and (1,0,A), wave 1 (0,0,P) and (1,0,P), waves 2 and 3 (1,1,A)
+    // and (1,1,P); acc[0] is the diagonal job, accumulated over the sub-block rounds.
+    const float2 g16 = *reinterpret_cast<const float2*>(Gref + (16 / REF) * 128 + c0);
+    if (w < 2) {  // right factors of the off-diagonal tile: rows 0..15, through row 16
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int r = 8 * w + i;
-        float x0 = 0.f, x1 = 0.f;
-        if (r <= lim) {
-          x0 = kn[i][0] * ex2(gm.x - G[i][0]);  // <= e^80
-          x1 = kn[i][1] * ex2(gm.y - G[i][1]);
-        }
         uint32_t h, l;
-        split2(x0, x1, h, l);
+        split2(kn[i][0] * ex2(g16.x - G[i][0]), kn[i][1] * ex2(g16.y - G[i][1]), h, l);  // <= 1
         const int o = (r * LDA + c0) * 2;
         *reinterpret_cast<uint32_t*>(X + xRh + o) = h;
         *reinterpret_cast<uint32_t*>(X + xRl + o) = l;
       }
     }
     __syncthreads();
-    if (mb >= 16 * jt && mb < 16 * jt + 16 && 16 * ja <= lim) {
-      const int row = 16 * jt + l16;
-      const bool rowin = (row >= mb) && (row <= lim);
-      const int col = 16 * ja + l16;
+    if (w < 2) {
+      const int row = 16 + l16, col = l16;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         const int ea = (row * LDA + 32 * kk + 8 * g4) * 2;
         const int eb = (col * LDA + 32 * kk + 8 * g4) * 2;
         const bf16x8 bh = ld_frag(X, xRh + eb), bl = ld_frag(X, xRl + eb);
-#pragma unroll
-        for (int jb = 0; jb < 2; ++jb) {
-          if (jb >= njobs) break;
-          const int mat = (w < 2) ? jb : (w - 2);
-          bf16x8 ah = ld_frag(X, (mat ? xLQh : xLKh) + ea), al = ld_frag(X, (mat ? xLQl : xLKl) + ea);
-          if (!rowin) { ah = bf16x8{}; al = bf16x8{}; }
-          acc[jb] = mfma(ah, bh, acc[jb]);
-          acc[jb] = mfma(ah, bl, acc[jb]);
-          acc[jb] = mfma(al, bh, acc[jb]);
-        }
+        const bf16x8 ah = ld_frag(X, (w ? xLQh : xLKh) + ea), al = ld_frag(X, (w ? xLQl : xLKl) + ea);
+        acc[1] = mfma(ah, bh, acc[1]);
+        acc[1] = mfma(ah, bl, acc[1]);
+        acc[1] = mfma(al, bh, acc[1]);
       }
     }
     __syncthreads();
+    if (w >= 2) {  // left factors of the lower half with their own sub-block references
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int r = 8 * w + i;
+        const float2 gm = *reinterpret_cast<const float2*>(Gref + (r / REF) * 128 + c0);
+        const float e0 = ex2(G[i][0] - gm.x), e1 = ex2(G[i][1] - gm.y);  // in [e^-80, 1]
+        uint32_t kh, kl, qh, ql;
+        split2(kn[i][0] * e0, kn[i][1] * e1, kh, kl);
+        split2(qn[i][0] * e0, qn[i][1] * e1, qh, ql);
+        const int o = (r * LDA + c0) * 2;
+        *reinterpret_cast<uint32_t*>(X + xLKh + o) = kh;
+        *reinterpret_cast<uint32_t*>(X + xLKl + o) = kl;
+        *reinterpret_cast<uint32_t*>(X + xLQh + o) = qh;
+        *reinterpret_cast<uint32_t*>(X + xLQl + o) = ql;
+      }
+    }
+    // Round b: sub-block b of both halves at once (rows 16t + b REF .. + REF - 1).
+    const int t = w >= 2 ? 1 : 0;  // this wave's half: its rows and its diagonal tile
+    for (int b = 0; b < 16 / REF; ++b) {
+      const int mb = 16 * t + b * REF;
+      const int lim = mb + REF - 1;  // right factors past the sub-block are 0
+      {
+        const float2 gm = *reinterpret_cast<const float2*>(Gref + (mb / REF) * 128 + c0);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int r = 8 * w + i;
+          float x0 = 0.f, x1 = 0.f;
+          if (r <= lim) {
+            x0 = kn[i][0] * ex2(gm.x - G[i][0]);  // <= e^80
+            x1 = kn[i][1] * ex2(gm.y - G[i][1]);
+          }
+          uint32_t h, l;
+          split2(x0, x1, h, l);
+          const int o = (r * LDA + c0) * 2;
+          *reinterpret_cast<uint32_t*>(X + xRh + o) = h;
+          *reinterpret_cast<uint32_t*>(X + xRl + o) = l;
+        }
+      }
+      __syncthreads();
+      {
+        const int row = 16 * t + l16;
+        const bool rowin = (row >= mb) && (row <= lim);
+        const int col = 16 * t + l16;
+        const int mat = w & 1;  // A (waves 0, 2) or P (waves 1, 3)
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const int ea = (row * LDA + 32 * kk + 8 * g4) * 2;
+          const int eb = (col * LDA + 32 * kk + 8 * g4) * 2;
+          const bf16x8 bh = ld_frag(X, xRh + eb), bl = ld_frag(X, xRl + eb);
+          bf16x8 ah = ld_frag(X, (mat ? xLQh : xLKh) + ea), al = ld_frag(X, (mat ? xLQl : xLKl) + ea);
+          if (!rowin) { ah = bf16x8{}; al = bf16x8{}; }
+          acc[0] = mfma(ah, bh, acc[0]);
+          acc[0] = mfma(ah, bl, acc[0]);
+          acc[0] = mfma(al, bh, acc[0]);
+        }
+      }
+      __syncthreads();
+    }
   }
   // Masked, scaled tiles: A strictly lower times beta_r, P lower with diagonal. The tile
   // above the diagonal is written as zeros.
@@ -468,12 +518,15 @@ __device__ void process_item(const Plan& p, const Item& it, const Inputs& in, ch
 #pragma unroll
     for (int jb = 0; jb < 2; ++jb) {
       if (jb >= njobs) break;
-      const int mat = (w < 2) ? jb : (w - 2);
+      // REF = 16: waves 0 and 1 hold both matrices of row tile w; below, one matrix of
+      // both row tiles (the layout of the sub-block rounds above).
+      const int mat = (w < 2) ? (REF == 16 ? jb : w) : (w - 2);
+      const int jtj = (w < 2) ? (REF == 16 ? jt : jb) : 1;
       float* dst = mat ? Ps : As;
       const int diag = mat;  // P keeps its diagonal, A does not
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int row = 16 * jt + 4 * g4 + i;
+        const int row = 16 * jtj + 4 * g4 + i;
         const float sc = mat ? p.scale : betas[row];
         dst[row * LDF + col] = (col < row + diag) ? sc * acc[jb][i] : 0.f;
       }
