@@ -126,7 +126,7 @@ def load() -> ctypes.CDLL:
     lib.kda_dv_split.restype = c_int32
     lib.kda_dv_split.argtypes = [c_int32, c_int32, c_int32]
     lib.kda_seg_len.restype = c_int32
-    lib.kda_seg_len.argtypes = [c_int32, c_int32, c_int64]
+    lib.kda_seg_len.argtypes = [c_int32, c_int32, c_int64, c_int32]
     lib.kda_ref_block.restype = c_int32
     lib.kda_ref_block.argtypes = [c_float]
     lib.kda_get_stats.restype = c_int

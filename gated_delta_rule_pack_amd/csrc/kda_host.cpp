@@ -243,10 +243,15 @@ int32_t dv_split_for(int32_t units_n, int32_t H, int32_t cus) {
 // Segment length of the segmented scan: only few, long sequences are split (many
 // (sequence, head) units already fill the chip, and below 256 chunks the maps and their
 // combination cost more than the shorter walk saves); about 8 segments for the longest
-// sequence, at least kSegMin chunks each.
-int32_t seg_len_for(int32_t N, int32_t H, int64_t max_chunks) {
+// sequence, at least kSegMin chunks each. Where 8 segments would already put the scan on
+// 64-channel slices (dv_split 2) and 10 still fit them on cus CUs, 10: the map and scan
+// walks shorten by a fifth for two more combine steps. cus = 0 gives the 8-segment length
+// (the longest walk, as validation checks it).
+int32_t seg_len_for(int32_t N, int32_t H, int64_t max_chunks, int32_t cus) {
   if ((int64_t)N * H > 96 || max_chunks < 256) return 0;
-  return (int32_t)std::max<int64_t>(kda::kSegMin, (max_chunks + 7) / 8);
+  const int64_t u = (int64_t)N * H;
+  const int64_t n = (u * 10 * 2 <= cus && u * 8 * 4 > cus) ? 10 : 8;
+  return (int32_t)std::max<int64_t>(kda::kSegMin, (max_chunks + n - 1) / n);
 }
 
 // The scan addresses one segment's chunk records through a buffer descriptor with a
@@ -492,7 +497,9 @@ int32_t kda_dv_split(int32_t n_seqs, int32_t H, int32_t cu_count) { return dv_sp
 
 int32_t kda_ref_block(float lower_bound) { return ref_block_for(lower_bound); }
 
-int32_t kda_seg_len(int32_t n_seqs, int32_t H, int64_t max_chunks) { return seg_len_for(n_seqs, H, max_chunks); }
+int32_t kda_seg_len(int32_t n_seqs, int32_t H, int64_t max_chunks, int32_t cu_count) {
+  return seg_len_for(n_seqs, H, max_chunks, cu_count);
+}
 
 kda_status kda_chunk_fwd_validate(const kda_fwd_args* a) {
   if (!a) return KDA_ERR_INVALID_ARG;
@@ -538,7 +545,7 @@ kda_status kda_chunk_fwd_validate(const kda_fwd_args* a) {
   if (a->cu_seqlens_host) {
     if (!bounds_ok(a->cu_seqlens_host, a->N, a->T)) return KDA_ERR_INVALID_ARG;
     const int64_t mc = max_seq_chunks(a->cu_seqlens_host, a->N);
-    const int32_t L = seg_len_for(a->N, a->H, mc);
+    const int32_t L = seg_len_for(a->N, a->H, mc, 0);  // the longest walk any device would take
     if (!walk_fits(L > 0 ? L : mc)) return KDA_ERR_UNSUPPORTED;
   }
   return KDA_OK;
@@ -701,7 +708,7 @@ kda_status kda_chunk_fwd(kda_ctx* ctx, const kda_fwd_args* a, void* ws, size_t w
   }
 
   const bool decode = max_seq_len(cu, a->N) <= 1 && !ctx->decode_off;
-  int seg_len = seg_len_for(a->N, a->H, max_seq_chunks(cu, a->N));
+  int seg_len = seg_len_for(a->N, a->H, max_seq_chunks(cu, a->N), ctx->cu_count);
   if (ctx->seg_len_override >= 0 && (int64_t)a->N * a->H <= 96) seg_len = ctx->seg_len_override;
   if (!decode && !walk_fits(seg_len > 0 ? seg_len : max_seq_chunks(cu, a->N))) return KDA_ERR_UNSUPPORTED;
   CacheEntry* e = nullptr;

@@ -227,13 +227,15 @@ kda_status kda_prepare_chunk_indices(const int32_t* cu_host, int32_t n_seqs, int
 int32_t kda_dv_split(int32_t n_seqs, int32_t H, int32_t cu_count);
 
 /* Segment length (chunks) of the segmented scan for n_seqs sequences of H heads whose
- * longest sequence has max_chunks chunks (host-only, pure); 0 = not segmented. The pages
- * split long sequences into segments (a pass that composes each segment, then a scan
- * over segments; aiter PR 5754, Technical Details and Test Result; segment tables built
- * from host bounds in the one metadata upload, aiter PR 6912, Changes). Here: only when
- * n_seqs*H <= 96 and max_chunks >= 256; about 8 segments for the longest sequence, at
- * least 8 chunks each. */
-int32_t kda_seg_len(int32_t n_seqs, int32_t H, int64_t max_chunks);
+ * longest sequence has max_chunks chunks, on cu_count compute units (host-only, pure);
+ * 0 = not segmented. The pages split long sequences into segments (a pass that composes
+ * each segment, then a scan over segments; aiter PR 5754, Technical Details and Test
+ * Result; segment tables built from host bounds in the one metadata upload, aiter PR
+ * 6912, Changes). Here: only when n_seqs*H <= 96 and max_chunks >= 256; about 8 segments
+ * for the longest sequence, at least 8 chunks each, or 10 when 8 would already take
+ * 64-channel slices (kda_dv_split 2) and 10 still do (n_seqs*H*10*2 <= cu_count <
+ * n_seqs*H*8*4). cu_count = 0 gives the 8-segment length. */
+int32_t kda_seg_len(int32_t n_seqs, int32_t H, int64_t max_chunks, int32_t cu_count);
 
 /* Reference-row block the prep kernel uses for a gate lower bound (host-only, pure): the
  * largest s in {16, 8, 4, 2, 1} with (s - 1) * |lower_bound| <= 80, so that every factor

@@ -217,14 +217,22 @@ def test_dv_split_and_ref_block_policies(lib):
 
 def test_segment_length_policy(lib):
     # Few long sequences: about 8 segments for the longest, at least 8 chunks each.
-    assert lib.kda_seg_len(1, 12, 512) == 64
-    assert lib.kda_seg_len(1, 12, 500) == 63
-    assert lib.kda_seg_len(8, 12, 256) == 32
+    assert lib.kda_seg_len(1, 12, 512, 0) == 64
+    assert lib.kda_seg_len(1, 16, 512, 256) == 64    # 10 segments would leave dv_split 2
+    assert lib.kda_seg_len(1, 8, 512, 256) == 64     # 8 segments still take dv_split 4
+    assert lib.kda_seg_len(8, 12, 256, 256) == 32
+    assert lib.kda_seg_len(4, 2, 301, 256) == 38
+    # 12 heads on 256 CUs: 8 segments already take dv_split 2 and 10 still do.
+    assert lib.kda_seg_len(1, 12, 512, 256) == 52
+    assert lib.kda_seg_len(1, 12, 500, 256) == 50
+    for L, H in ((52, 12),):
+        segs = -(-512 // L)
+        assert segs == 10 and lib.kda_dv_split(segs, H, 256) == 2
     # Short sequences, or enough (sequence, head) units already: not segmented.
-    assert lib.kda_seg_len(1, 12, 128) == 0
-    assert lib.kda_seg_len(1, 12, 255) == 0
-    assert lib.kda_seg_len(9, 12, 1000) == 0
-    assert lib.kda_seg_len(128, 12, 64) == 0
+    assert lib.kda_seg_len(1, 12, 128, 256) == 0
+    assert lib.kda_seg_len(1, 12, 255, 256) == 0
+    assert lib.kda_seg_len(9, 12, 1000, 256) == 0
+    assert lib.kda_seg_len(128, 12, 64, 256) == 0
 
 
 # ---------------------------------------------------------------- fake runtime
@@ -484,7 +492,7 @@ def test_segmented_call_launches_and_tables(lib, fake):
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     N, T, H = len(lens), int(cu[-1]), 2
     a, _, _ = _valid_args(bufs, T=T, N=N, H=H, cu=cu, paged=True)
-    L = lib.kda_seg_len(N, H, 301)
+    L = lib.kda_seg_len(N, H, 301, 256)
     assert L == 38
     assert _call(lib, fake, a) == _lib.KDA_OK
     assert fake.launches == [(0, 0x10), (2, 0x10), (3, 0x10), (1, 0x10)]
@@ -641,5 +649,5 @@ def test_validation_rejects_record_walk_beyond_32_bits(lib):
         cu = np.array([0, T], np.int32)
         a.T = T
         a.cu_seqlens_host = cu.ctypes.data
-        assert lib.kda_seg_len(1, 1, -(-T // 32)) > 0
+        assert lib.kda_seg_len(1, 1, -(-T // 32), 0) > 0
         assert lib.kda_chunk_fwd_validate(ctypes.byref(a)) == want, T
