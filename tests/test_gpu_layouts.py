@@ -66,6 +66,19 @@ def test_grouped_heads_paged_matches_oracle(H, H_qk):
     _say(f"  out {e_out:.3e} state {e_state:.3e}")
 
 
+@pytest.mark.parametrize("lb,shift", [(-8.0, 0.0), (-20.0, 6.0), (-100.0, 0.0)])
+def test_grouped_heads_steep_gates(lb, shift):
+    """Grouped heads with steep gates: the grouped instantiations of the sub-block rounds
+    (reference blocks 8, 4 and 1) against the oracle."""
+    wl = make_workload("gva_steep", LENGTHS, H=6, H_qk=2, seed=44, state_mode="paged", num_slots=9,
+                       has_initial="bernoulli", stride_pad=64, lower_bound=lb, gate_shift=shift)
+    _say(f"case {wl.name} lb={lb} shift={shift}")
+    run = run_gpu(wl)
+    e_out, e_state = compare(wl, run)
+    untouched_slots_bitwise(wl, run)
+    _say(f"  out {e_out:.3e} state {e_state:.3e}")
+
+
 @pytest.mark.parametrize("lengths", [LENGTHS, [1, 0, 1, 1]], ids=["chunked", "decode"])
 def test_grouped_heads_equal_repeated_heads(lengths):
     wl = make_workload("gva_rep", lengths, H=6, H_qk=2, seed=42, state_mode="dense", state_dtype="bf16")

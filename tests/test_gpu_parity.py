@@ -58,12 +58,15 @@ def test_no_state_mode():
     _say(f"  out {e_out:.3e}")
 
 
-def test_bf16_gate_and_beta_inputs():
+@pytest.mark.parametrize("lb,shift", [(-5.0, 0.0), (-20.0, 6.0)])
+def test_bf16_gate_and_beta_inputs(lb, shift):
+    """bf16 raw gate and beta, with the default gate and a steep one (4-row reference
+    blocks, the bf16-gate instantiation of the sub-block rounds)."""
     wl = make_workload("bf16_raw", [77, 33], H=2, seed=14, state_mode="dense", gate_dtype="bf16",
-                       beta_dtype="bf16")
+                       beta_dtype="bf16", lower_bound=lb, gate_shift=shift)
     run = run_gpu(wl)
     e_out, e_state = compare(wl, run)
-    _say(f"  out {e_out:.3e} state {e_state:.3e}")
+    _say(f"  lb {lb}: out {e_out:.3e} state {e_state:.3e}")
 
 
 @pytest.mark.parametrize("lb,shift", [(-5.0, 6.0), (-8.0, 0.0), (-8.0, 6.0), (-20.0, 6.0), (-40.0, 0.0),
