@@ -23,10 +23,11 @@ KDA_ERR_ALIAS = 5
 KDA_ERR_WORKSPACE = 6
 KDA_ERR_CAPTURE_MISS = 7
 KDA_ERR_HIP = 8
+KDA_ERR_NO_SPACE = 9
 STATUS_NAMES = {
     0: "KDA_OK", 1: "KDA_ERR_INVALID_ARG", 2: "KDA_ERR_UNSUPPORTED", 3: "KDA_ERR_STATE_MODE",
     4: "KDA_ERR_STRIDE", 5: "KDA_ERR_ALIAS", 6: "KDA_ERR_WORKSPACE", 7: "KDA_ERR_CAPTURE_MISS",
-    8: "KDA_ERR_HIP",
+    8: "KDA_ERR_HIP", 9: "KDA_ERR_NO_SPACE",
 }
 
 # kda_dtype
@@ -58,6 +59,7 @@ class Stats(Structure):
         ("last_dv_split", c_int32), ("last_ref_block", c_int32), ("last_n_chunks", c_int64),
         ("last_seg_len", c_int32), ("last_n_segments", c_int32),
         ("last_path", c_int32), ("reserved", c_int32),
+        ("arena_grows", c_uint64), ("arena_device_bytes", c_uint64), ("arena_host_bytes", c_uint64),
     ]
 
     def as_dict(self):

@@ -18,8 +18,8 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <map>
 #include <new>
-#include <unordered_map>
 #include <vector>
 
 #include "kda.h"
@@ -126,7 +126,8 @@ inline int segments_of(int64_t nc, int seg_len) {
 
 // Layout of the single int32 metadata buffer: token bounds [N+1], chunk offsets [N+1],
 // chunk table [n_chunks][2], segment table [n_seg][kSegInts], map-slot -> segment
-// [n_maps], multi-segment sequences [n_multi][4].
+// [n_maps], multi-segment sequences [n_multi][4] (sequence, first map slot, maps, slot of
+// the first segment's start state).
 Meta meta_layout(const int32_t* cu, int N, int seg_len) {
   Meta m;
   m.N = N;
@@ -193,12 +194,17 @@ void build_meta(const int32_t* cu, const Meta& m, int32_t* buf) {
       table[2 * c + 1] = j;
     }
     const int G = segments_of(nc, m.seg_len);
+    // Start-state slots: slot j < n_maps holds the state after map slot j; slot n_maps + k
+    // holds the initial state of the k-th multi-segment sequence, copied there (fp32) by
+    // the combine kernel. A multi-segment sequence's last segment writes the final state
+    // into the caller's plane (its slot, for a pool) from another workgroup of the scan
+    // launch than its first segment, so no segment of such a sequence reads that plane.
     for (int g = 0; g < G; ++g, ++s) {
       int32_t* e = seg + (size_t)kda::kSegInts * s;
       e[0] = i;                                              // sequence
       e[1] = g * m.seg_len;                                  // first chunk (within the sequence)
       e[2] = G == 1 ? nc : std::min(m.seg_len, nc - g * m.seg_len);  // chunks
-      e[3] = g == 0 ? -1 : mbase + g - 1;                    // map slot holding the start state
+      e[3] = g > 0 ? mbase + g - 1 : (G > 1 ? m.n_maps + k : -1);  // start-state slot (-1: the caller's)
       e[4] = g == G - 1 ? -1 : mbase + g;                    // map slot this segment produces
       if (g < G - 1) m2s[mbase + g] = s;
     }
@@ -206,6 +212,7 @@ void build_meta(const int32_t* cu, const Meta& m, int32_t* buf) {
       comb[4 * k] = i;
       comb[4 * k + 1] = mbase;
       comb[4 * k + 2] = G - 1;
+      comb[4 * k + 3] = m.n_maps + k;  // start-state slot of the sequence's first segment
       ++k;
     }
     mbase += G - 1;
@@ -277,30 +284,45 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 }  // namespace
 
 // ------------------------------------------------------------------ context
+// First-fit sub-allocator over blocks of device or pinned host memory. The context makes
+// one block of each kind when it is created. A request that fits nowhere, even after the
+// completed releases have been taken back, adds a block, except in an allocation-free
+// call. Blocks are freed only when the context is destroyed: hipFree and hipHostFree
+// synchronise the device, so no call frees memory.
+struct Arena {
+  struct Block {
+    char* base = nullptr;
+    size_t bytes = 0;
+    std::map<size_t, size_t> free;  // offset -> length of each free range, coalesced
+  };
+  bool device = true;
+  std::vector<Block> blocks;
+  size_t total = 0;
+};
+
+// A range that goes back to its arena once every event in it has completed, i.e. once
+// the work that reads it (an upload, the kernels of the calls that used an evicted
+// metadata buffer) has finished.
+struct Release {
+  Arena* arena = nullptr;
+  void* ptr = nullptr;
+  size_t bytes = 0;
+  std::vector<void*> events;       // plain events, back to their pool afterwards
+  std::vector<void*> completions;  // launch-attached completion events, back to their pool
+};
+
 struct CacheEntry {
   std::vector<int32_t> bounds;  // key: the full bounds array and the segment length
   int seg_len = 0;
   uint64_t hash = 0;
-  void* dev = nullptr;          // device metadata buffer
+  void* dev = nullptr;          // device metadata buffer (a range of the device arena)
   size_t bytes = 0;
   Meta meta;
-  void* upload_event = nullptr;
+  void* upload_event = nullptr;  // recorded right after the upload
   void* upload_stream = nullptr;
-  std::vector<std::pair<void*, void*>> uses;  // (stream, event recorded after the last use)
-  bool retained = false;                      // used under graph capture: never freed early
+  std::vector<std::pair<void*, void*>> uses;  // (stream, completion event of the last launch there)
+  bool retained = false;                      // used under graph capture: never evicted
   uint64_t tick = 0;
-};
-
-struct Staging {
-  void* host = nullptr;
-  size_t bytes = 0;
-  void* event = nullptr;  // recorded after the copy out of this buffer
-  bool used = false;
-};
-
-struct Graveyard {
-  void* dev;
-  std::vector<std::pair<void*, void*>> uses;
 };
 
 struct ProfileMarks {
@@ -318,11 +340,10 @@ struct kda_ctx {
   std::vector<ProfileMarks> marks_free;  // reusable
   int cu_count = 0;
   std::vector<CacheEntry*> cache;
-  std::vector<Graveyard> graveyard;
-  std::vector<Staging> ring;
-  size_t ring_next = 0;
-  void* bounds_host = nullptr;  // pinned landing area for bounds read-backs
-  size_t bounds_host_bytes = 0;
+  Arena dev_arena, host_arena;
+  std::vector<Release> releases;  // in release order
+  std::vector<void*> ev_pool, cev_pool;  // idle plain and completion events
+  std::vector<int32_t> bounds_tmp;       // bounds read back from the device
   uint64_t tick = 0;
   kda_stats stats{};
 };
@@ -330,69 +351,189 @@ struct kda_ctx {
 namespace {
 
 constexpr size_t kCacheCap = 64;
-constexpr size_t kRingSlots = 32;
+constexpr size_t kArenaAlign = 256;
+constexpr size_t kDevArenaBytes = size_t(4) << 20;   // first device block (metadata buffers)
+constexpr size_t kHostArenaBytes = size_t(4) << 20;  // first pinned block (upload staging)
 
 kda_status hip_fail() { return KDA_ERR_HIP; }
 
-void release_events(kda_ctx* ctx, std::vector<std::pair<void*, void*>>& uses) {
-  for (auto& u : uses) ctx->rt.event_destroy(ctx->rt.user, u.second);
-  uses.clear();
-}
+inline size_t round_arena(size_t n) { return (n + kArenaAlign - 1) / kArenaAlign * kArenaAlign; }
 
-bool uses_done(kda_ctx* ctx, const std::vector<std::pair<void*, void*>>& uses) {
-  for (auto& u : uses)
-    if (ctx->rt.event_query(ctx->rt.user, u.second) != 0) return false;
-  return true;
-}
-
-// Free evicted buffers whose last uses have completed (never waits).
-void sweep_graveyard(kda_ctx* ctx) {
-  auto& gy = ctx->graveyard;
-  for (size_t i = 0; i < gy.size();) {
-    if (uses_done(ctx, gy[i].uses)) {
-      release_events(ctx, gy[i].uses);
-      ctx->rt.device_free(ctx->rt.user, gy[i].dev);
-      gy[i] = gy.back();
-      gy.pop_back();
-    } else {
-      ++i;
+void* arena_take(Arena& a, size_t bytes) {
+  bytes = round_arena(bytes);
+  for (auto& b : a.blocks)
+    for (auto it = b.free.begin(); it != b.free.end(); ++it) {
+      if (it->second < bytes) continue;
+      const size_t off = it->first, len = it->second;
+      b.free.erase(it);
+      if (len > bytes) b.free.emplace(off + bytes, len - bytes);
+      return b.base + off;
     }
+  return nullptr;
+}
+
+void arena_give(Arena& a, void* p, size_t bytes) {
+  bytes = round_arena(bytes);
+  char* c = static_cast<char*>(p);
+  for (auto& b : a.blocks) {
+    if (c < b.base || c >= b.base + b.bytes) continue;
+    size_t off = (size_t)(c - b.base);
+    auto next = b.free.lower_bound(off);
+    if (next != b.free.end() && off + bytes == next->first) {
+      bytes += next->second;
+      next = b.free.erase(next);
+    }
+    if (next != b.free.begin()) {
+      auto prev = std::prev(next);
+      if (prev->first + prev->second == off) {
+        prev->second += bytes;
+        return;
+      }
+    }
+    b.free.emplace(off, bytes);
+    return;
   }
 }
 
-void evict_one(kda_ctx* ctx) {
-  // Least recently used entry that is not retained.
+kda_status arena_add_block(kda_ctx* ctx, Arena& a, size_t want) {
+  const size_t last = a.blocks.empty() ? 0 : a.blocks.back().bytes;
+  const size_t bytes = round_arena(std::max(want, 2 * last));
+  void* p = nullptr;
+  const int rc = a.device ? ctx->rt.device_alloc(ctx->rt.user, &p, bytes)
+                          : ctx->rt.host_alloc_pinned(ctx->rt.user, &p, bytes);
+  if (rc || !p) return hip_fail();
+  Arena::Block b;
+  b.base = static_cast<char*>(p);
+  b.bytes = bytes;
+  b.free.emplace(0, bytes);
+  a.blocks.push_back(std::move(b));
+  a.total += bytes;
+  return KDA_OK;
+}
+
+kda_status ev_get(kda_ctx* ctx, bool completion, void** ev) {
+  auto& pool = completion ? ctx->cev_pool : ctx->ev_pool;
+  if (!pool.empty()) {
+    *ev = pool.back();
+    pool.pop_back();
+    return KDA_OK;
+  }
+  const int rc = completion ? ctx->rt.event_create_completion(ctx->rt.user, ev) : ctx->rt.event_create(ctx->rt.user, ev);
+  return rc ? hip_fail() : KDA_OK;
+}
+
+bool release_done(kda_ctx* ctx, const Release& r) {
+  for (void* e : r.events)
+    if (ctx->rt.event_query(ctx->rt.user, e) != 0) return false;
+  for (void* e : r.completions)
+    if (ctx->rt.event_query(ctx->rt.user, e) != 0) return false;
+  return true;
+}
+
+void finish_release(kda_ctx* ctx, Release& r) {
+  arena_give(*r.arena, r.ptr, r.bytes);
+  ctx->ev_pool.insert(ctx->ev_pool.end(), r.events.begin(), r.events.end());
+  ctx->cev_pool.insert(ctx->cev_pool.end(), r.completions.begin(), r.completions.end());
+}
+
+// Take back every range whose readers have completed (queries only, never waits).
+void sweep(kda_ctx* ctx) {
+  auto& rs = ctx->releases;
+  size_t w = 0;
+  for (size_t i = 0; i < rs.size(); ++i) {
+    if (release_done(ctx, rs[i])) {
+      finish_release(ctx, rs[i]);
+    } else {
+      if (w != i) rs[w] = std::move(rs[i]);  // (a self-move would empty the event lists)
+      ++w;
+    }
+  }
+  rs.resize(w);
+}
+
+// Allocation-free calls only: wait for the oldest pending release of arena a (one counted
+// blocking wait) and take it back. *waited is false when none is pending.
+kda_status wait_oldest(kda_ctx* ctx, Arena& a, bool* waited) {
+  *waited = false;
+  auto& rs = ctx->releases;
+  for (size_t i = 0; i < rs.size(); ++i) {
+    if (rs[i].arena != &a) continue;
+    for (void* e : rs[i].events)
+      if (ctx->rt.event_synchronize(ctx->rt.user, e)) return hip_fail();
+    for (void* e : rs[i].completions)
+      if (ctx->rt.event_synchronize(ctx->rt.user, e)) return hip_fail();
+    ctx->stats.blocking_syncs++;
+    finish_release(ctx, rs[i]);
+    rs.erase(rs.begin() + i);
+    *waited = true;
+    return KDA_OK;
+  }
+  return KDA_OK;
+}
+
+bool evict_one(kda_ctx* ctx);
+
+// A range of `bytes` from arena a. may_grow: add a block when nothing fits (never waits).
+// Otherwise (allocation-free calls) wait for pending releases, evicting cached metadata
+// when the device arena is full of it; KDA_ERR_NO_SPACE when the request cannot fit.
+kda_status arena_alloc(kda_ctx* ctx, Arena& a, size_t bytes, bool may_grow, void** out) {
+  for (;;) {
+    if ((*out = arena_take(a, bytes))) return KDA_OK;
+    sweep(ctx);
+    if ((*out = arena_take(a, bytes))) return KDA_OK;
+    if (may_grow) {
+      if (kda_status st = arena_add_block(ctx, a, bytes)) return st;
+      ctx->stats.arena_grows++;
+      continue;
+    }
+    bool waited = false;
+    if (kda_status st = wait_oldest(ctx, a, &waited)) return st;
+    if (waited) continue;
+    if (&a == &ctx->dev_arena && evict_one(ctx)) continue;
+    return KDA_ERR_NO_SPACE;
+  }
+}
+
+// Move the least recently used entry that is not retained to the release list; false when
+// every entry is retained (or the cache is empty).
+bool evict_one(kda_ctx* ctx) {
   int victim = -1;
   for (size_t i = 0; i < ctx->cache.size(); ++i) {
     if (ctx->cache[i]->retained) continue;
     if (victim < 0 || ctx->cache[i]->tick < ctx->cache[victim]->tick) victim = (int)i;
   }
-  if (victim < 0) return;
+  if (victim < 0) return false;
   CacheEntry* e = ctx->cache[victim];
-  Graveyard g{e->dev, std::move(e->uses)};
-  if (e->upload_event) g.uses.push_back({e->upload_stream, e->upload_event});
-  ctx->graveyard.push_back(std::move(g));
+  Release r;
+  r.arena = &ctx->dev_arena;
+  r.ptr = e->dev;
+  r.bytes = e->bytes;
+  if (e->upload_event) r.events.push_back(e->upload_event);
+  for (auto& u : e->uses) r.completions.push_back(u.second);
+  ctx->releases.push_back(std::move(r));
   ctx->cache.erase(ctx->cache.begin() + victim);
   delete e;
+  return true;
 }
 
-// The completion event that tracks this entry's last use on a stream (created on the first
+// The completion event that tracks this entry's last use on a stream (taken on the first
 // use there). The call's last kernel records it on completion, so an evicted buffer is
-// freed only after every launch that read it has finished.
+// reused only after every launch that read it has finished.
 kda_status use_event(kda_ctx* ctx, CacheEntry* e, void* stream, void** ev) {
   for (auto& u : e->uses)
     if (u.first == stream) {
       *ev = u.second;
       return KDA_OK;
     }
-  if (ctx->rt.event_create_completion(ctx->rt.user, ev)) return hip_fail();
+  if (kda_status st = ev_get(ctx, true, ev)) return st;
   e->uses.push_back({stream, *ev});
   return KDA_OK;
 }
 
-// Find or upload the metadata for these bounds.
-kda_status get_meta(kda_ctx* ctx, const int32_t* cu, int N, int seg_len, void* stream, CacheEntry** out,
-                    int& capturing) {
+// Find or upload the metadata for these bounds. may_grow: the arenas may add blocks
+// (false in allocation-free calls).
+kda_status get_meta(kda_ctx* ctx, const int32_t* cu, int N, int seg_len, void* stream, bool may_grow,
+                    CacheEntry** out, int& capturing) {
   capturing = 0;
   if (ctx->rt.stream_is_capturing(ctx->rt.user, stream, &capturing)) return hip_fail();
   const uint64_t hsh = hash_bounds(cu, N);
@@ -415,54 +556,51 @@ kda_status get_meta(kda_ctx* ctx, const int32_t* cu, int N, int seg_len, void* s
   }
   if (capturing) return KDA_ERR_CAPTURE_MISS;
 
-  sweep_graveyard(ctx);
-  while (ctx->cache.size() >= kCacheCap) {
-    const size_t before = ctx->cache.size();
-    evict_one(ctx);
-    if (ctx->cache.size() == before) break;  // everything retained
-  }
+  sweep(ctx);
+  while (ctx->cache.size() >= kCacheCap)
+    if (!evict_one(ctx)) break;  // everything retained
   const Meta m = meta_layout(cu, N, seg_len);
   const size_t bytes = m.words * sizeof(int32_t);
 
-  // Pinned staging slot: reuse only once its previous copy has completed.
-  Staging& st = ctx->ring[ctx->ring_next];
-  ctx->ring_next = (ctx->ring_next + 1) % ctx->ring.size();
-  if (st.used && ctx->rt.event_query(ctx->rt.user, st.event) != 0) {
-    if (ctx->rt.event_synchronize(ctx->rt.user, st.event)) return hip_fail();
-    ctx->stats.blocking_syncs++;
-  }
-  if (st.bytes < bytes) {
-    if (st.host) ctx->rt.host_free_pinned(ctx->rt.user, st.host);
-    st.host = nullptr;
-    st.bytes = 0;
-    const size_t want = std::max<size_t>(bytes, 4096);
-    if (ctx->rt.host_alloc_pinned(ctx->rt.user, &st.host, want)) return hip_fail();
-    st.bytes = want;
-  }
-  build_meta(cu, m, reinterpret_cast<int32_t*>(st.host));
-
+  // Pinned staging and the device buffer, both sub-allocated; the staging range goes back
+  // once its copy has completed.
+  void* stage = nullptr;
+  if (kda_status st = arena_alloc(ctx, ctx->host_arena, bytes, may_grow, &stage)) return st;
   CacheEntry* e = new (std::nothrow) CacheEntry();
-  if (!e) return KDA_ERR_HIP;
+  if (!e) {
+    arena_give(ctx->host_arena, stage, bytes);
+    return KDA_ERR_HIP;
+  }
+  if (kda_status st = arena_alloc(ctx, ctx->dev_arena, bytes, may_grow, &e->dev)) {
+    arena_give(ctx->host_arena, stage, bytes);
+    delete e;
+    return st;
+  }
+  build_meta(cu, m, reinterpret_cast<int32_t*>(stage));
   e->bounds.assign(cu, cu + N + 1);
   e->seg_len = seg_len;
   e->hash = hsh;
   e->meta = m;
   e->bytes = bytes;
-  if (ctx->rt.device_alloc(ctx->rt.user, &e->dev, bytes)) {
+  void* stage_ev = nullptr;
+  if (ev_get(ctx, false, &e->upload_event) || ev_get(ctx, false, &stage_ev) ||
+      ctx->rt.memcpy_h2d_async(ctx->rt.user, e->dev, stage, bytes, stream) ||
+      ctx->rt.event_record(ctx->rt.user, e->upload_event, stream) ||
+      ctx->rt.event_record(ctx->rt.user, stage_ev, stream)) {
+    // Nothing reads the ranges if the copy was not enqueued; if it was, they stay held
+    // (the copy may still run) until the context is destroyed.
+    if (e->upload_event) ctx->ev_pool.push_back(e->upload_event);
+    if (stage_ev) ctx->ev_pool.push_back(stage_ev);
     delete e;
     return hip_fail();
   }
-  if (ctx->rt.event_create(ctx->rt.user, &e->upload_event) ||
-      ctx->rt.memcpy_h2d_async(ctx->rt.user, e->dev, st.host, bytes, stream) ||
-      ctx->rt.event_record(ctx->rt.user, e->upload_event, stream)) {
-    ctx->rt.device_free(ctx->rt.user, e->dev);
-    delete e;
-    return hip_fail();
-  }
+  Release r;
+  r.arena = &ctx->host_arena;
+  r.ptr = stage;
+  r.bytes = bytes;
+  r.events.push_back(stage_ev);
+  ctx->releases.push_back(std::move(r));
   e->upload_stream = stream;
-  if (!st.event && ctx->rt.event_create(ctx->rt.user, &st.event)) return hip_fail();
-  if (ctx->rt.event_record(ctx->rt.user, st.event, stream)) return hip_fail();
-  st.used = true;
   e->tick = ++ctx->tick;
   ctx->cache.push_back(e);
   ctx->stats.cache_misses++;
@@ -489,6 +627,7 @@ const char* kda_status_str(kda_status s) {
     case KDA_ERR_WORKSPACE: return "workspace missing or too small";
     case KDA_ERR_CAPTURE_MISS: return "metadata cache miss during stream capture";
     case KDA_ERR_HIP: return "HIP runtime error";
+    case KDA_ERR_NO_SPACE: return "the call does not fit the fixed memory it may use";
   }
   return "unknown status";
 }
@@ -555,23 +694,29 @@ kda_status kda_chunk_fwd_validate(const kda_fwd_args* a);
 
 namespace {
 
-// Workspace: chunk records, then (when the call may be segmented) the segment maps and
-// the segment start states. Chunks over all sequences are at most ceil(T / 32) + N; a
-// segmented call has at most max_chunks / kSegMin maps.
+// Workspace: chunk records, then the segment maps, then the segment start states (one
+// per map, for the segment after it, and one per multi-segment sequence, for its first
+// segment).
 struct WsLayout {
   size_t records = 0, maps = 0, starts = 0, total = 0;
 };
 
-WsLayout ws_layout(const kda_fwd_args* a) {
+WsLayout ws_layout_for(int H, int64_t records, int64_t maps, int64_t multi) {
   WsLayout w;
-  const int64_t max_chunks = ((int64_t)a->T + kChunk - 1) / kChunk + a->N;
-  w.records = (size_t)a->H * (size_t)max_chunks * kda::kRecBytes;
-  int64_t max_maps = 0;
-  if ((int64_t)a->N * a->H <= 96) max_maps = max_chunks / kda::kSegMin;
+  w.records = (size_t)H * (size_t)records * kda::kRecBytes;
   w.maps = w.records;
-  w.starts = w.maps + (size_t)max_maps * a->H * kda::kMapBytes;
-  w.total = w.starts + (size_t)max_maps * a->H * kda::kStartBytes;
+  w.starts = w.maps + (size_t)maps * H * kda::kMapBytes;
+  w.total = w.starts + (size_t)(maps + multi) * H * kda::kStartBytes;
   return w;
+}
+
+// The caller's workspace, from T, N and H alone: chunks over all sequences are at most
+// ceil(T / 32) + N; only a call with N * H <= 96 may be segmented, with at most
+// max_chunks / kSegMin maps and no more multi-segment sequences than maps.
+WsLayout ws_layout(const kda_fwd_args* a) {
+  const int64_t max_chunks = ((int64_t)a->T + kChunk - 1) / kChunk + a->N;
+  const int64_t max_maps = (int64_t)a->N * a->H <= 96 ? max_chunks / kda::kSegMin : 0;
+  return ws_layout_for(a->H, max_chunks, max_maps, max_maps);
 }
 
 }  // namespace
@@ -619,7 +764,12 @@ kda_status kda_ctx_create_with_runtime(const kda_runtime* rt, int cu_count, kda_
     const int v = std::atoi(e);
     if (v == 0 || v >= kda::kSegMin) ctx->seg_len_override = v;
   }
-  ctx->ring.resize(kRingSlots);
+  ctx->dev_arena.device = true;
+  ctx->host_arena.device = false;
+  if (arena_add_block(ctx, ctx->dev_arena, kDevArenaBytes) || arena_add_block(ctx, ctx->host_arena, kHostArenaBytes)) {
+    kda_ctx_destroy(ctx);
+    return KDA_ERR_HIP;
+  }
   *out = ctx;
   return KDA_OK;
 }
@@ -635,39 +785,34 @@ kda_status kda_ctx_create(int device, kda_ctx** out) {
 void kda_ctx_destroy(kda_ctx* ctx) {
   if (!ctx) return;
   auto& rt = ctx->rt;
+  std::vector<void*> evs = ctx->ev_pool, cevs = ctx->cev_pool;
   for (CacheEntry* e : ctx->cache) {
-    if (e->upload_event) rt.event_synchronize(rt.user, e->upload_event);
-    for (auto& u : e->uses) rt.event_synchronize(rt.user, u.second);
-    release_events(ctx, e->uses);
-    if (e->upload_event) rt.event_destroy(rt.user, e->upload_event);
-    rt.device_free(rt.user, e->dev);
+    if (e->upload_event) evs.push_back(e->upload_event);
+    for (auto& u : e->uses) cevs.push_back(u.second);
     delete e;
+  }
+  for (auto& r : ctx->releases) {
+    evs.insert(evs.end(), r.events.begin(), r.events.end());
+    cevs.insert(cevs.end(), r.completions.begin(), r.completions.end());
   }
   for (auto* v : {&ctx->marks, &ctx->marks_free})
     for (auto& m : *v)
-      for (void* e : m.ev) {
-        rt.event_synchronize(rt.user, e);
-        rt.event_destroy(rt.user, e);
-      }
-  for (auto& g : ctx->graveyard) {
-    for (auto& u : g.uses) rt.event_synchronize(rt.user, u.second);
-    release_events(ctx, g.uses);
-    rt.device_free(rt.user, g.dev);
-  }
-  for (auto& s : ctx->ring) {
-    if (s.event) {
-      rt.event_synchronize(rt.user, s.event);
-      rt.event_destroy(rt.user, s.event);
-    }
-    if (s.host) rt.host_free_pinned(rt.user, s.host);
-  }
-  if (ctx->bounds_host) rt.host_free_pinned(rt.user, ctx->bounds_host);
+      for (void* e : m.ev) evs.push_back(e);
+  // Every event is waited for before the memory its work reads is freed.
+  for (auto* v : {&evs, &cevs})
+    for (void* e : *v) rt.event_synchronize(rt.user, e);
+  for (auto* v : {&evs, &cevs})
+    for (void* e : *v) rt.event_destroy(rt.user, e);
+  for (auto& b : ctx->dev_arena.blocks) rt.device_free(rt.user, b.base);
+  for (auto& b : ctx->host_arena.blocks) rt.host_free_pinned(rt.user, b.base);
   delete ctx;
 }
 
 kda_status kda_get_stats(const kda_ctx* ctx, kda_stats* out) {
   if (!ctx || !out) return KDA_ERR_INVALID_ARG;
   *out = ctx->stats;
+  out->arena_device_bytes = ctx->dev_arena.total;
+  out->arena_host_bytes = ctx->host_arena.total;
   return KDA_OK;
 }
 
@@ -677,33 +822,41 @@ kda_status kda_reset_stats(kda_ctx* ctx) {
   return KDA_OK;
 }
 
-kda_status kda_chunk_fwd(kda_ctx* ctx, const kda_fwd_args* a, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// One forward call. alloc_free: ws is a fixed device area of ws_bytes that must hold the
+// call's exact workspace (else KDA_ERR_NO_SPACE), and the metadata arenas may not grow;
+// otherwise ws is the caller's workspace of at least kda_chunk_fwd_workspace_bytes().
+kda_status chunk_fwd_impl(kda_ctx* ctx, const kda_fwd_args* a, void* ws, size_t ws_bytes, void* stream,
+                          bool alloc_free) {
   if (!ctx) return KDA_ERR_INVALID_ARG;
   kda_status st = kda_chunk_fwd_validate(a);
   if (st != KDA_OK) return st;
-  const size_t need = kda_chunk_fwd_workspace_bytes(a);
-  if (need > 0 && (!ws || ws_bytes < need || !aligned(ws, 256))) return KDA_ERR_WORKSPACE;
+  if (!alloc_free) {
+    const size_t need = ws_layout(a).total;
+    if (need > 0 && (!ws || ws_bytes < need || !aligned(ws, 256))) return KDA_ERR_WORKSPACE;
+  }
   auto& rt = ctx->rt;
 
-  // Host bounds: given, or read back once (one counted synchronisation).
+  // Host bounds: given, or read back once (one counted synchronisation) into a range of
+  // the pinned arena, taken back right after the wait.
   const int32_t* cu = a->cu_seqlens_host;
   if (!cu) {
     int capturing = 0;
     if (rt.stream_is_capturing(rt.user, stream, &capturing)) return hip_fail();
     if (capturing) return KDA_ERR_CAPTURE_MISS;  // a read-back cannot run under capture
     const size_t bytes = (size_t)(a->N + 1) * sizeof(int32_t);
-    if (ctx->bounds_host_bytes < bytes) {
-      if (ctx->bounds_host) rt.host_free_pinned(rt.user, ctx->bounds_host);
-      ctx->bounds_host = nullptr;
-      ctx->bounds_host_bytes = 0;
-      if (rt.host_alloc_pinned(rt.user, &ctx->bounds_host, bytes)) return hip_fail();
-      ctx->bounds_host_bytes = bytes;
-    }
-    if (rt.memcpy_d2h_async(rt.user, ctx->bounds_host, a->cu_seqlens, bytes, stream)) return hip_fail();
-    if (rt.stream_synchronize(rt.user, stream)) return hip_fail();
+    void* land = nullptr;
+    if ((st = arena_alloc(ctx, ctx->host_arena, bytes, !alloc_free, &land)) != KDA_OK) return st;
+    if (rt.memcpy_d2h_async(rt.user, land, a->cu_seqlens, bytes, stream) || rt.stream_synchronize(rt.user, stream))
+      return hip_fail();  // the range stays held: the copy may not have completed
     ctx->stats.blocking_syncs++;
     ctx->stats.d2h_reads++;
-    cu = reinterpret_cast<const int32_t*>(ctx->bounds_host);
+    ctx->bounds_tmp.assign(reinterpret_cast<const int32_t*>(land), reinterpret_cast<const int32_t*>(land) + a->N + 1);
+    arena_give(ctx->host_arena, land, bytes);
+    cu = ctx->bounds_tmp.data();
     if (!bounds_ok(cu, a->N, a->T)) return KDA_ERR_INVALID_ARG;
   }
 
@@ -711,11 +864,21 @@ kda_status kda_chunk_fwd(kda_ctx* ctx, const kda_fwd_args* a, void* ws, size_t w
   int seg_len = seg_len_for(a->N, a->H, max_seq_chunks(cu, a->N), ctx->cu_count);
   if (ctx->seg_len_override >= 0 && (int64_t)a->N * a->H <= 96) seg_len = ctx->seg_len_override;
   if (!decode && !walk_fits(seg_len > 0 ? seg_len : max_seq_chunks(cu, a->N))) return KDA_ERR_UNSUPPORTED;
+  WsLayout wl;
+  if (alloc_free) {
+    // The exact workspace of this call (a decode call needs none).
+    if (!decode) {
+      const Meta m = meta_layout(cu, a->N, seg_len);
+      wl = ws_layout_for(a->H, m.n_chunks, m.n_maps, m.n_multi);
+    }
+    if (wl.total > ws_bytes || (wl.total > 0 && (!ws || !aligned(ws, 256)))) return KDA_ERR_NO_SPACE;
+  } else {
+    wl = ws_layout(a);
+  }
   CacheEntry* e = nullptr;
   int capturing = 0;
-  st = get_meta(ctx, cu, a->N, seg_len, stream, &e, capturing);
+  st = get_meta(ctx, cu, a->N, seg_len, stream, !alloc_free, &e, capturing);
   if (st != KDA_OK) return st;
-  const WsLayout wl = ws_layout(a);
 
   kda::Plan p{};
   p.T = a->T;
@@ -811,6 +974,14 @@ kda_status kda_chunk_fwd(kda_ctx* ctx, const kda_fwd_args* a, void* ws, size_t w
   ctx->stats.last_n_segments = e->meta.n_seg;
   ctx->stats.last_path = decode ? 1 : 0;
   return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_chunk_fwd(kda_ctx* ctx, const kda_fwd_args* a, void* ws, size_t ws_bytes, void* stream) {
+  return chunk_fwd_impl(ctx, a, ws, ws_bytes, stream, false);
 }
 
 kda_status kda_profile_enable(kda_ctx* ctx, int enable) {

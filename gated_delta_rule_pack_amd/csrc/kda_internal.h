@@ -38,7 +38,8 @@ static_assert(kRecBytes % 256 == 0, "records stay 256-byte aligned");
 // every segment's start state, and the scan then runs all segments in parallel.
 constexpr int kSegMin = 8;        // shortest segment (chunks)
 constexpr int kSegInts = 8;       // segment table record: sequence, first chunk, chunks,
-                                  // start-state map slot (-1: the call's initial state),
+                                  // start-state slot (-1: the caller's initial state, read
+                                  // only by a sequence's single segment),
                                   // own map slot (-1: last segment, writes the final state)
 constexpr size_t kMapBytes = (size_t)2 * kHead * kHead * 4;  // A (bf16 hi, lo), C (fp32), [k][v] each
 constexpr size_t kStartBytes = (size_t)kHead * kHead * 4;    // start state, fp32, [v][k]
@@ -66,7 +67,8 @@ struct Plan {
   int n_seg, n_maps, n_multi, seg_len;
   const int32_t* d_seg;    // [n_seg][kSegInts] segment table (device)
   const int32_t* d_m2s;    // [n_maps] segment of each map slot (device)
-  const int32_t* d_comb;   // [n_multi][4] (sequence, first map slot, maps, 0) (device)
+  const int32_t* d_comb;   // [n_multi][4] (sequence, first map slot, maps, start slot of
+                           // the first segment) (device)
   int state_dtype;
   const void* state_in;
   int in_mode;
@@ -79,7 +81,9 @@ struct Plan {
   void* ws;             // first chunk record (256-byte aligned)
   float* maps;          // [n_maps][H] segment maps: A as bf16 hi and lo planes, then C fp32,
                         // each [K][V] (S^T layout)
-  float* starts;        // [n_maps][H][V][K] state at the start of the segment after map slot m
+  float* starts;        // [n_maps + n_multi][H][V][K] fp32 start states: slot m < n_maps
+                        // starts the segment after map slot m, slot n_maps + k the first
+                        // segment of multi-segment sequence k (its initial state)
   int cu_count;         // compute units of the device (persistent grid sizing)
 };
 

@@ -65,7 +65,7 @@ struct HeadLds {
 struct Unit {
   int n, h, grp;
   int c0, nch;         // first chunk within the sequence, chunks
-  int m_prev, m_self;  // scan: start-state map slot (-1: initial state), own map slot
+  int m_prev, m_self;  // scan: start-state slot (-1: the caller's initial state), own map slot
                        // (-1: last segment); map: the map slot
 };
 

@@ -13,7 +13,8 @@
 // file forms A and C for every segment but a sequence's last. This kernel walks, per
 // (sequence, head, 32 value rows), S_{g+1} = S_g A_g + C_g over the sequence's segments
 // from the call's initial state, in fp32 (bf16 hi/lo operand splits on MFMA), and stores
-// the results: the start states the scan runs the segments from.
+// the results: the start states the scan runs the segments from, the first segment's
+// included (a copy of the initial state).
 
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
@@ -42,11 +43,16 @@ __global__ __launch_bounds__(256) void segcombine_kernel(Plan p) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, g4 = lane >> 4, l16 = lane & 15;
 
-  // Initial state rows (the call's initial state, or zero).
+  // Initial state rows (the call's initial state, or zero). They are also stored, in fp32
+  // (exact for every storage dtype), as the start state of the sequence's first segment:
+  // the scan must not read the caller's plane for a sequence whose last segment writes
+  // the final state into it from another workgroup of the same launch.
   const void* in_plane = state_in_plane<SDT>(p, n, h);
+  float* first = p.starts + ((size_t)cb[3] * p.H + h) * kHead * kHead;
   for (int q = threadIdx.x; q < 32 * 32; q += 256) {
     const int r = q >> 5, c4 = (q & 31) * 4;
     const f32x4 x = in_plane ? load_state4_vk<SDT>(in_plane, 32 * slice + r, c4, p.kfirst) : zero4();
+    *reinterpret_cast<f32x4*>(first + (size_t)(32 * slice + r) * kHead + c4) = x;
 #pragma unroll
     for (int i = 0; i < 4; ++i) split_bf16(x[i], Shi[r * kLdS + c4 + i], Slo[r * kLdS + c4 + i]);
   }

@@ -26,8 +26,9 @@
  *
  * Conventions for every function below:
  *  - Pointers are device memory owned by the caller unless marked "host".
- *  - The library never allocates or frees caller memory. It owns only its context:
- *    pinned staging buffers and a device-side metadata cache.
+ *  - The library never allocates or frees caller memory. It owns only its context: a
+ *    pinned staging arena and a device arena for the metadata cache, both made when the
+ *    context is created and freed only when it is destroyed.
  *  - Tensors are contiguous row-major with the shapes stated; "[T, H, D]" means
  *    element (t, h, d) sits at offset (t * H + h) * D + d.
  *  - A failed call returns before enqueuing any work: nothing is written.
@@ -55,7 +56,9 @@ typedef enum kda_status {
   KDA_ERR_ALIAS = 5,        /* the byte ranges of out and v overlap */
   KDA_ERR_WORKSPACE = 6,    /* workspace null or smaller than kda_chunk_fwd_workspace_bytes() */
   KDA_ERR_CAPTURE_MISS = 7, /* metadata-cache miss while the stream is being captured */
-  KDA_ERR_HIP = 8           /* a HIP runtime call or a kernel launch failed */
+  KDA_ERR_HIP = 8,          /* a HIP runtime call or a kernel launch failed */
+  KDA_ERR_NO_SPACE = 9      /* a call that may not allocate: its workspace or metadata does not
+                               fit the fixed memory it must use */
 } kda_status;
 
 /* Element types accepted by the arguments that allow a choice. */
@@ -123,7 +126,8 @@ typedef struct kda_stats {
   uint64_t calls;          /* successful kda_chunk_fwd calls */
   uint64_t cache_hits;     /* metadata found in the cache (no upload) */
   uint64_t cache_misses;   /* metadata built and uploaded */
-  uint64_t blocking_syncs; /* host waits on the device: bounds read-backs and staging reuse */
+  uint64_t blocking_syncs; /* host waits on the device: bounds read-backs, and (calls that may
+                              not allocate) waits for arena ranges still being read */
   uint64_t d2h_reads;      /* bounds read back because cu_seqlens_host was null */
   uint64_t h2d_uploads;    /* asynchronous metadata uploads */
   int32_t last_dv_split;   /* value-channel split used by the last scan launch */
@@ -133,6 +137,9 @@ typedef struct kda_stats {
   int32_t last_n_segments; /* segments (over all sequences) in the last call */
   int32_t last_path;       /* kernels of the last call: 0 = prep + scan, 1 = decode */
   int32_t reserved;        /* zero */
+  uint64_t arena_grows;        /* blocks added to the metadata arenas after context creation */
+  uint64_t arena_device_bytes; /* device memory the metadata arena holds (not reset) */
+  uint64_t arena_host_bytes;   /* pinned host memory the staging arena holds (not reset) */
 } kda_stats;
 
 typedef struct kda_ctx kda_ctx;
@@ -175,20 +182,40 @@ typedef struct kda_runtime {
   int (*event_create_completion)(void* user, void** event);
 } kda_runtime;
 
-/* Context: device properties (CU count), pinned staging ring, metadata cache, stats.
- * device is a HIP device ordinal. Returns KDA_ERR_UNSUPPORTED on a device that is not
- * gfx950. One context may be used from one host thread at a time. */
+/* Context (aiter PR 6912, Changes: metadata built from host bounds, uploaded with one
+ * non-blocking copy from pinned memory and cached on the bounds' contents; a hit from
+ * another stream waits on the uploading stream; a buffer used under graph capture lives
+ * as long as its owner). It holds the device properties (CU count), a content-keyed cache
+ * of up to 64 metadata buffers, the arenas they and their pinned staging are sub-allocated
+ * from, and the stats. kda_ctx_create makes a 4 MiB device block and a 4 MiB pinned block;
+ * a call whose metadata does not fit in their free ranges adds a block (arena_grows in
+ * kda_stats), and no call frees memory (hipFree and hipHostFree synchronise the device):
+ * a range is reused once the work that reads it has completed. device is a HIP device
+ * ordinal. Returns KDA_ERR_UNSUPPORTED on a device that is not gfx950 and KDA_ERR_HIP if
+ * an allocation fails. One context may be used from one host thread at a time (the Python
+ * binding serialises its calls on a shared context). */
 kda_status kda_ctx_create(int device, kda_ctx** out);
 kda_status kda_ctx_create_with_runtime(const kda_runtime* rt, int cu_count, kda_ctx** out);
-/* Waits for the context's outstanding uploads, then frees what it owns. */
+/* Waits for every event the context still tracks (uploads, the launches that read its
+ * metadata buffers), then frees the arenas and everything else it owns. Null is a no-op. */
 void kda_ctx_destroy(kda_ctx* ctx);
 
-/* Host-only, pure: bytes of caller workspace one call with these shapes needs
- * (depends on T, N, H only: chunk records, plus room for segment maps and start states
- * when N*H <= 96). 0 when the arguments are invalid. */
+/* Host-only, pure: bytes of caller workspace one call with these shapes needs. The pages
+ * keep the prefill's intermediates in one workspace pool (aiter PR 4741, Optimizations
+ * Applied); here it holds one 35 328-byte record per (head, chunk) that prep writes and
+ * the scan reads, and, when N*H <= 96 (a call that may be segmented), room for segment maps
+ * (128 KiB per map and head) and fp32 start states (64 KiB per segment start and head). It
+ * depends on T, N and H only. 0 when the arguments are invalid (kda_chunk_fwd_validate). */
 size_t kda_chunk_fwd_workspace_bytes(const kda_fwd_args* args);
 
-/* Host-only: every argument check kda_chunk_fwd makes, touching no device memory. */
+/* Host-only: every argument check kda_chunk_fwd makes, touching no device memory (aiter PR
+ * 5754, Technical Details and its review thread: a pool slot plane must be dense and
+ * stride(0) may pad but not be smaller than one H*V*K plane, KDA_ERR_STRIDE; out must not
+ * alias v, KDA_ERR_ALIAS; dense and paged state are mutually exclusive and a pool returns
+ * no final_state, KDA_ERR_STATE_MODE; state_indices are not checked, since that would need
+ * the device). Also: K = V = 128, the dtypes above, finite scale, lower_bound <= 0, 16-byte
+ * aligned token tensors and state planes, H_qk dividing H, and host bounds (when given)
+ * that start at 0, end at T and never decrease. Returns the first failing check's code. */
 kda_status kda_chunk_fwd_validate(const kda_fwd_args* args);
 
 /* Forward call. Validates, resolves metadata (cache hit, or one asynchronous upload from
@@ -264,7 +291,15 @@ kda_status kda_profile_calls(kda_ctx* ctx, float* call_ms, int64_t cap, int64_t*
 size_t kda_fwd_args_size(void);
 size_t kda_stats_size(void);
 
+/* A static string naming a status code ("unknown status" for other values): the error
+ * conventions the codes carry follow aiter PR 5754, Technical Details (rejected stride,
+ * aliasing out, conflicting state modes) and aiter PR 6912, Changes (a metadata miss under
+ * graph capture is an error). */
 const char* kda_status_str(kda_status status);
+/* Copies the context's counters (aiter PR 6912, Tests: a call with host bounds makes no
+ * synchronising call on a metadata-cache miss, the same call with device bounds does;
+ * blocking_syncs and d2h_reads count exactly those waits). KDA_ERR_INVALID_ARG for null
+ * pointers. kda_reset_stats zeroes every counter except the arena sizes. */
 kda_status kda_get_stats(const kda_ctx* ctx, kda_stats* out);
 kda_status kda_reset_stats(kda_ctx* ctx);
 

@@ -3,7 +3,7 @@ and the host orchestration driven through a recording fake runtime.
 
 The fake runtime stands in for HIP: "device" memory is host memory, copies are memmoves,
 events are integers whose completion the test controls, and kernel launches are only
-recorded. This exercises the metadata cache, the pinned staging ring, the no-sync
+recorded. This exercises the metadata cache, the device and pinned arenas, the no-sync
 contract with host bounds and the capture rules without a GPU.
 """
 import ctypes
@@ -168,11 +168,12 @@ def test_workspace_bytes(lib):
         if T == 0:
             a.q = a.k = a.v = a.g_raw = a.beta_raw = a.out = None
         max_chunks = (T + 31) // 32 + N
-        # Records; then, when the call may be segmented (N*H <= 96), room for the maps and
-        # start states of segments of at least 8 chunks.
+        # Records; then, when the call may be segmented (N*H <= 96), room for the maps of
+        # segments of at least 8 chunks and two start states per map (the segment after it;
+        # at most as many multi-segment sequences, whose first segments get one each).
         want = H * max_chunks * REC
         if N * H <= 96:
-            want += (max_chunks // 8) * H * (MAP_BYTES + START_BYTES)
+            want += (max_chunks // 8) * H * (MAP_BYTES + 2 * START_BYTES)
         assert lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(a)) == want
 
 
@@ -357,6 +358,7 @@ def fake(lib):
     ctx = ctypes.c_void_p()
     assert lib.kda_ctx_create_with_runtime(ctypes.byref(f.rt), 256, ctypes.byref(ctx)) == _lib.KDA_OK
     f.ctx = ctx
+    f.creation_log, f.log = f.log, []
     yield f
     lib.kda_ctx_destroy(ctx)
 
@@ -465,21 +467,25 @@ def test_one_token_calls_take_the_decode_kernel(lib, fake):
 
 def _segments_reference(cu, L):
     """Segments of each sequence: runs of L chunks (the last shorter), one empty segment
-    for an empty sequence; map slots numbered over all segments but each sequence's last."""
+    for an empty sequence; map slots numbered over all segments but each sequence's last.
+    Start-state slots: the segment after map slot m starts from slot m; the first segment
+    of the k-th multi-segment sequence from slot n_maps + k (a copy of the initial state);
+    only a single-segment sequence reads the caller's state (-1)."""
+    counts = [-(-(int(cu[n + 1]) - int(cu[n])) // 32) for n in range(len(cu) - 1)]
+    groups = [1 if nc <= L else -(-nc // L) for nc in counts]
+    n_maps = sum(G - 1 for G in groups)
     segs, m2s, comb, mbase = [], [], [], 0
-    for n in range(len(cu) - 1):
-        nc = -(-(int(cu[n + 1]) - int(cu[n])) // 32)
-        G = 1 if nc <= L else -(-nc // L)
+    for n, (nc, G) in enumerate(zip(counts, groups)):
         for g in range(G):
             c0 = g * L
             nch = nc if G == 1 else min(L, nc - c0)
-            m_prev = -1 if g == 0 else mbase + g - 1
+            m_prev = mbase + g - 1 if g > 0 else (n_maps + len(comb) if G > 1 else -1)
             m_self = -1 if g == G - 1 else mbase + g
             if m_self >= 0:
                 m2s.append(len(segs))
             segs.append([n, c0, nch, m_prev, m_self, 0, 0, 0])
         if G > 1:
-            comb.append([n, mbase, G - 1, 0])
+            comb.append([n, mbase, G - 1, n_maps + len(comb)])
         mbase += G - 1
     return np.array(segs, np.int32), np.array(m2s, np.int32), np.array(comb, np.int32).reshape(-1, 4)
 
@@ -516,6 +522,16 @@ def test_segmented_call_launches_and_tables(lib, fake):
         nc = -(-lens[n] // 32)
         assert mine[0, 1] == 0 and mine[:, 2].sum() == nc
         assert np.all(mine[1:, 1] == mine[:-1, 1] + mine[:-1, 2])
+    # Only a sequence with a single segment reads the caller's state in the scan: the last
+    # segment of a longer one writes that plane from another workgroup of the same launch.
+    uploaded = words[off_seg:off_seg + 8 * len(segs)].reshape(-1, 8)
+    for n in range(N):
+        mine = uploaded[uploaded[:, 0] == n]
+        if len(mine) > 1:
+            assert np.all(mine[:, 3] >= 0), (n, mine[:, 3])
+            assert len(set(mine[:, 3].tolist())) == len(mine)
+    n_maps = len(m2s)
+    assert sorted(comb[:, 3].tolist()) == list(range(n_maps, n_maps + len(comb)))
 
 
 def test_unsegmented_table_lists_longest_sequences_first(lib, fake):
@@ -588,28 +604,58 @@ def test_cross_stream_hit_waits_on_upload(lib, fake):
     assert fake.syncs() == []
 
 
-def test_cache_eviction_frees_only_completed_buffers(lib, fake):
+def test_context_creation_makes_one_block_of_each_arena(lib, fake):
+    assert sorted(e[0] for e in fake.creation_log) == ["dev_alloc", "host_alloc"]
+    st = _stats(lib, fake)
+    assert st["arena_device_bytes"] == 4 << 20 and st["arena_host_bytes"] == 4 << 20
+    assert st["arena_grows"] == 0
+
+
+def test_misses_behind_pending_work_neither_wait_nor_allocate(lib, fake):
+    """Serving with new bounds every call while the device is still busy: 200 misses whose
+    work never completes evict cached buffers (the cache holds 64) and keep every staging
+    range, yet no call waits, allocates or frees (aiter PR 6912, Tests)."""
     bufs = FakeBufs()
-    for i in range(70):  # more than the cache holds
+    for i in range(200):
         b, _, _ = _valid_args(bufs, T=50 + i, N=1, cu=np.array([0, 50 + i], np.int32))
         assert _call(lib, fake, b) == _lib.KDA_OK
-    # Nothing completed yet: evicted buffers wait in the graveyard, none freed, no syncs.
-    assert [e for e in fake.log if e[0] == "dev_free"] == []
-    assert fake.syncs() == [] or all(e[0] == "event_sync" for e in fake.syncs())
+    kinds = [e[0] for e in fake.log]
+    assert fake.syncs() == []
+    assert not {"dev_alloc", "host_alloc", "dev_free", "host_free"} & set(kinds)
+    st = _stats(lib, fake)
+    assert st["cache_misses"] == 200 and st["blocking_syncs"] == 0 and st["arena_grows"] == 0
+
+
+def test_arena_ranges_come_back_only_after_their_readers_complete(lib, fake):
+    """An evicted metadata buffer and a staging range are reused only once the events of
+    the work that reads them have completed; until then new ranges come from elsewhere."""
+    bufs = FakeBufs()
+    dsts = []
+    for i in range(70):  # more than the cache holds: six evictions, nothing completed
+        b, _, _ = _valid_args(bufs, T=50 + i, N=1, cu=np.array([0, 50 + i], np.int32))
+        assert _call(lib, fake, b) == _lib.KDA_OK
+        dsts.append(fake.uploads[-1][0])
+    assert len(set(dsts)) == 70  # every upload went to a distinct device range
     fake.complete_all()
     b, _, _ = _valid_args(bufs, T=999, N=1, cu=np.array([0, 999], np.int32))
     assert _call(lib, fake, b) == _lib.KDA_OK
-    assert len([e for e in fake.log if e[0] == "dev_free"]) >= 6
+    assert fake.uploads[-1][0] in dsts[:6]  # a range of an evicted, completed buffer
+    assert not {"dev_alloc", "dev_free"} & set(e[0] for e in fake.log)
 
 
-def test_staging_reuse_waits_only_when_copy_pending(lib, fake):
+def test_metadata_larger_than_the_arena_adds_a_block(lib, fake):
+    """A call whose metadata exceeds the free ranges adds one block to each arena (no
+    frees, no waits)."""
     bufs = FakeBufs()
-    for i in range(40):  # more misses than staging slots, none completed
-        b, _, _ = _valid_args(bufs, T=10 + i, N=1, cu=np.array([0, 10 + i], np.int32))
-        assert _call(lib, fake, b) == _lib.KDA_OK
+    N = 300_000  # (N + 1) * 2 + chunk table + segment table: about 16 MB of metadata
+    cu = np.arange(N + 1, dtype=np.int32) * 2
+    a, _, _ = _valid_args(bufs, T=int(cu[-1]), N=N, H=1, cu=cu)
+    assert _call(lib, fake, a) == _lib.KDA_OK
+    kinds = [e[0] for e in fake.log]
+    assert kinds.count("dev_alloc") == 1 and kinds.count("host_alloc") == 1
+    assert fake.syncs() == [] and "dev_free" not in kinds
     st = _stats(lib, fake)
-    assert st["blocking_syncs"] == 40 - 32  # one wait per reuse of a busy slot
-    assert st["cache_misses"] == 40
+    assert st["arena_grows"] == 2 and st["arena_device_bytes"] >= 8 << 20
 
 
 def test_workspace_too_small_is_rejected_before_any_work(lib, fake):
