@@ -18,7 +18,7 @@ import torch
 
 import gated_delta_rule_pack_amd as kda
 from gated_delta_rule_pack_amd.workloads import HEAD_DIM, make_workload, to_f64
-from tests.kda_harness import compare, gpu_final_states, run_gpu, untouched_slots_bitwise
+from tests.kda_harness import GpuRun, compare, gpu_final_states, run_gpu, untouched_slots_bitwise
 
 pytestmark = pytest.mark.gpu
 
@@ -132,3 +132,27 @@ def test_non_default_stream():
     torch.cuda.synchronize()
     assert np.array_equal(_bits(ref.out), _bits(other.out))
     assert np.array_equal(_bits(ref.final_state), _bits(other.final_state))
+
+
+def test_side_stream_call_owns_its_allocations():
+    """A call on a side stream allocates its output and its temporary workspace on that
+    stream: an allocation of the same size on the current stream, written at once, cannot
+    land on memory the side stream's kernels still read or write."""
+    wl = make_workload("side_stream", [500, 300], H=4, seed=71, state_mode="dense")
+    d = {n: getattr(wl, n).cuda() for n in ("q", "k", "v", "g_raw", "beta_raw", "cu_seqlens", "initial_state")}
+    a = kda.make_args(d["q"], d["k"], d["v"], d["g_raw"], d["beta_raw"], d["cu_seqlens"], cu_seqlens_cpu=wl.cu_seqlens,
+                      initial_state=d["initial_state"], out=torch.empty_like(d["v"]))
+    need = kda.workspace_bytes(a)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        torch.cuda._sleep(20_000_000)  # keep the side stream busy while the host goes on
+    out, fin = kda.chunk_fwd(d["q"], d["k"], d["v"], d["g_raw"], d["beta_raw"], d["cu_seqlens"],
+                             cu_seqlens_cpu=wl.cu_seqlens, scale=wl.scale, initial_state=d["initial_state"],
+                             output_final_state=True, stream=side)
+    junk = [torch.empty(need, dtype=torch.uint8, device="cuda").fill_(0xFF),
+            torch.empty_like(d["v"]).fill_(float("nan")), torch.empty_like(d["initial_state"]).fill_(float("nan"))]
+    side.synchronize()
+    torch.cuda.synchronize()
+    del junk
+    compare(wl, GpuRun(to_f64(out[0]), to_f64(fin), None))

@@ -1,14 +1,17 @@
 """GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
 
-Bars: output rel-L2 <= 5e-3; final state rel-L2 <= 5e-3 with fp32 state storage and
-<= 1e-2 with fp16 / bf16 storage. Sizes: small cases run the whole oracle (several
-chunks and a ragged tail); the full-size workloads compare every output of a sample of
-heads or sequences the oracle can afford, plus properties checked on everything.
+Bars, per (sequence, head): output rel-L2 <= 5e-3; every output row within 2.5e-2 of
+the oracle (relative to its (sequence, head)'s RMS row at least); final state rel-L2
+<= 5e-3 with fp32 state storage and <= 1e-2 with fp16 / bf16 storage. Small cases span
+several chunks and a ragged tail; the full-size workloads (1 x 4096, 1 x 16384, the
+128-sequence batch, 256 one-token sequences) compare every head and every sequence, the
+oracle pooled over heads.
 """
 import numpy as np
 import pytest
 import torch
 
+import gated_delta_rule_pack_amd as kda
 from gated_delta_rule_pack_amd.workloads import standard, make_workload
 from tests.kda_harness import compare, run_gpu, untouched_slots_bitwise
 
@@ -90,41 +93,51 @@ def test_paged_1x4096_H12_full():
     _say(f"  out {e_out:.3e} state {e_state:.3e}")
 
 
-def test_paged_1x16384_H12_padded_stride_sampled_heads():
+def test_paged_1x16384_H12_padded_stride_all_heads():
+    """The segmented path at its real shape (10 segments x 12 heads, 64-channel slices):
+    every head and every output row against the oracle."""
     wl = standard("paged_1x16384_H12_pad")
     _say(f"case {wl.name}")
     run = run_gpu(wl)
-    assert np.all(np.isfinite(run.out))
-    e_out, e_state = compare(wl, run, heads=[0, 7])
+    compare(wl, run)
     untouched_slots_bitwise(wl, run)
-    _say(f"  heads 0,7: out {e_out:.3e} state {e_state:.3e}")
 
 
 @pytest.mark.parametrize("lb,shift", [(-5.0, 6.0), (-20.0, 6.0)])
-def test_1x16384_saturated_gates_nan_free(lb, shift):
-    """~160 nats (lb -5, raw +6) and ~640 nats (lb -20) of decay per chunk stay NaN-free."""
+def test_1x16384_saturated_gates_all_heads(lb, shift):
+    """~160 nats (lb -5, raw +6) and ~640 nats (lb -20) of decay per chunk: NaN-free and on
+    the oracle on every head."""
     wl = standard("paged_1x16384_H12_pad", gate_shift=shift, lower_bound=lb)
     _say(f"case {wl.name} lb={lb} shift={shift}")
     run = run_gpu(wl)
     assert np.all(np.isfinite(run.out))
-    e_out, e_state = compare(wl, run, heads=[3])
-    _say(f"  head 3: out {e_out:.3e} state {e_state:.3e}")
+    compare(wl, run)
 
 
-def test_varlen128_sampled_sequences():
+@pytest.mark.parametrize("T", [4096, 8192])
+@pytest.mark.parametrize("lb,shift", [(-1.0, -4.0), (0.0, 0.0)])
+def test_weak_and_no_decay_full_size(T, lb, shift):
+    """Weak decay (lb -1, raw gate -4: about 0.02 nats per token and channel) and no decay
+    at all (lb 0): the state keeps everything it has accumulated, so rounding in the scan
+    is not forgotten. 1 x 4096 (unsegmented, 16-channel slices) and 1 x 8192 (segmented),
+    12 heads, every head."""
+    wl = standard("paged_1x4096_H12", lengths=[T], lower_bound=lb, gate_shift=shift)
+    _say(f"case 1x{T} H12 lb={lb} shift={shift}")
+    ctx = kda.get_context("cuda")
+    run = run_gpu(wl)
+    _say(f"  segment length {ctx.stats()['last_seg_len']}")
+    compare(wl, run)
+
+
+def test_varlen128_all_sequences():
+    """128 sequences (0..2048 tokens, 4 empty, mixed flags, NaN-poisoned unflagged slots):
+    every sequence and head against the oracle."""
     wl = standard("paged_varlen128_H12")
-    lens = wl.info["lengths"]
-    flags = wl.has_initial_state.tolist()
-    empties = [i for i, x in enumerate(lens) if x == 0][:2]
-    no_init = [i for i, f in enumerate(flags) if not f and lens[i] > 0][:3]
-    longest = [int(np.argmax(lens))]
-    sample = sorted(set(empties + no_init + longest + [0, 1, len(lens) - 1]))
-    _say(f"case {wl.name} T={wl.T} sample={sample}")
+    _say(f"case {wl.name} T={wl.T}")
     run = run_gpu(wl)
     assert np.all(np.isfinite(run.out))
-    e_out, e_state = compare(wl, run, seqs=sample)
+    compare(wl, run)
     untouched_slots_bitwise(wl, run)
-    _say(f"  out {e_out:.3e} state {e_state:.3e}")
 
 
 @pytest.mark.parametrize("state_dtype", ["bf16", "f16"])

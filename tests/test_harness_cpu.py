@@ -1,0 +1,34 @@
+"""CPU checks of the parity harness itself: the per-head pooled oracle gives exactly what
+one direct oracle call over all heads gives (grouped heads, a paged pool with mixed
+flags, a subset of sequences), so the GPU tests compare against the oracle proper."""
+import numpy as np
+import pytest
+
+from gated_delta_rule_pack_amd.workloads import make_workload, to_f64
+from oracle import kda_forward
+from tests.kda_harness import run_oracle
+
+
+@pytest.mark.parametrize("workers", [0, 2])
+@pytest.mark.parametrize("mode", ["paged", "dense", "none"])
+def test_pooled_oracle_equals_direct_call(workers, mode):
+    wl = make_workload("harness", [37, 0, 70, 5], H=4, H_qk=2, seed=5, state_mode=mode, num_slots=6,
+                       stride_pad=16, has_initial="bernoulli", state_dtype="bf16" if mode == "paged" else "f32")
+    seqs = [0, 2, 3]
+    kw = {}
+    if mode == "paged":
+        kw = dict(state_cache=to_f64(wl.cache_view()), state_indices=wl.state_indices.numpy(),
+                  has_initial_state=wl.has_initial_state.numpy())
+    elif mode == "dense":
+        kw = dict(initial_state=to_f64(wl.initial_state))
+    ref_out, ref_fin = kda_forward(to_f64(wl.q[0]), to_f64(wl.k[0]), to_f64(wl.v[0]), to_f64(wl.g_raw[0]),
+                                   to_f64(wl.beta_raw[0]), wl.cu_seqlens.numpy(), scale=wl.scale,
+                                   lower_bound=wl.lower_bound, seqs=seqs, **kw)
+    heads = [3, 0, 1]
+    out, fin = run_oracle(wl, seqs=seqs, heads=heads, workers=workers)
+    cu = wl.cu_seqlens.numpy()
+    rows = np.concatenate([np.arange(cu[n], cu[n + 1]) for n in seqs])
+    assert np.array_equal(out[rows], ref_out[rows][:, heads])
+    assert np.all(np.isnan(np.delete(out, rows, axis=0)))
+    for n in seqs:
+        assert np.array_equal(fin[n], ref_fin[n][heads])
