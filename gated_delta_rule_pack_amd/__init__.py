@@ -13,7 +13,7 @@ from typing import Optional
 
 from . import _lib
 
-__all__ = ["chunk_fwd", "Context", "get_context", "workspace_bytes", "KDAError"]
+__all__ = ["chunk_fwd", "chunk_fwd_noalloc", "Context", "get_context", "workspace_bytes", "KDAError"]
 
 
 class KDAError(RuntimeError):
@@ -84,6 +84,11 @@ class Context:
         with self.lock:
             return int(_lib.load().kda_chunk_fwd(self.ptr, ctypes.byref(args), ctypes.c_void_p(workspace_ptr),
                                                  ctypes.c_size_t(workspace_bytes), ctypes.c_void_p(stream_ptr)))
+
+    def forward_noalloc(self, args: _lib.FwdArgs, stream_ptr: int) -> int:
+        """``kda_chunk_fwd_noalloc`` on this context (the status code)."""
+        with self.lock:
+            return int(_lib.load().kda_chunk_fwd_noalloc(self.ptr, ctypes.byref(args), ctypes.c_void_p(stream_ptr)))
 
     def close(self) -> None:
         with self.lock:
@@ -311,4 +316,38 @@ def chunk_fwd(q, k, v, g_raw, beta_raw, cu_seqlens, *, cu_seqlens_cpu=None, scal
     rc = ctx.forward(a, workspace.data_ptr(), workspace.numel(), stream.cuda_stream)
     if rc != _lib.KDA_OK:
         raise KDAError(rc, "kda_chunk_fwd")
+    return out, final_state
+
+
+def chunk_fwd_noalloc(q, k, v, g_raw, beta_raw, cu_seqlens, *, out, cu_seqlens_cpu=None, scale=None,
+                      lower_bound=-5.0, initial_state=None, final_state=None, state_cache=None,
+                      state_indices=None, has_initial_state=None, stream=None, context=None,
+                      state_k_first=False):
+    """:func:`chunk_fwd` through the allocation-free entry point (``kda_chunk_fwd_noalloc``).
+
+    Nothing is allocated, by torch or by the library: the caller passes ``out`` and, for a
+    dense final state, ``final_state`` (``[N, H, V, K]``, the initial state's dtype, else
+    fp32), and the library uses its fixed per-device workspace
+    (``kda_noalloc_scratch_bytes()``, 64 MiB). Calls on one GPU share that workspace, so
+    calls that overlap in time on one GPU race; a call that does not fit raises
+    :class:`KDAError` with ``KDA_ERR_NO_SPACE``. Returns ``(out, final_state)``.
+    """
+    import torch
+    device = q.device
+    if device.type != "cuda":
+        raise ValueError("inputs must be on a GPU")
+    for name, t in (("k", k), ("v", v), ("g_raw", g_raw), ("beta_raw", beta_raw), ("cu_seqlens", cu_seqlens),
+                    ("initial_state", initial_state), ("final_state", final_state), ("state_cache", state_cache),
+                    ("state_indices", state_indices), ("has_initial_state", has_initial_state), ("out", out)):
+        _check_dev(name, t, device)
+    a = make_args(q, k, v, g_raw, beta_raw, cu_seqlens, cu_seqlens_cpu=cu_seqlens_cpu, scale=scale,
+                  lower_bound=lower_bound, initial_state=initial_state, final_state=final_state,
+                  state_cache=state_cache, state_indices=state_indices,
+                  has_initial_state=has_initial_state, out=out, state_k_first=state_k_first)
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    ctx = context if context is not None else get_context(device)
+    rc = ctx.forward_noalloc(a, stream.cuda_stream)
+    if rc != _lib.KDA_OK:
+        raise KDAError(rc, "kda_chunk_fwd_noalloc")
     return out, final_state

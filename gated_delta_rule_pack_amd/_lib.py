@@ -123,6 +123,10 @@ def load() -> ctypes.CDLL:
     lib.kda_chunk_fwd_validate.argtypes = [POINTER(FwdArgs)]
     lib.kda_chunk_fwd.restype = c_int
     lib.kda_chunk_fwd.argtypes = [P, POINTER(FwdArgs), P, c_size_t, P]
+    lib.kda_chunk_fwd_noalloc.restype = c_int
+    lib.kda_chunk_fwd_noalloc.argtypes = [P, POINTER(FwdArgs), P]
+    lib.kda_noalloc_scratch_bytes.restype = c_size_t
+    lib.kda_noalloc_scratch_bytes.argtypes = []
     lib.kda_prepare_chunk_indices.restype = c_int
     lib.kda_prepare_chunk_indices.argtypes = [P, c_int32, c_int32, P, c_int64, POINTER(c_int64)]
     lib.kda_dv_split.restype = c_int32
@@ -160,7 +164,8 @@ def status_str(code: int) -> str:
 # Symbols include/kda.h declares (checked by the CPU tests).
 EXPORTS = [
     "kda_ctx_create", "kda_ctx_create_with_runtime", "kda_ctx_destroy",
-    "kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd_validate", "kda_chunk_fwd",
+    "kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd_validate", "kda_chunk_fwd", "kda_chunk_fwd_noalloc",
+    "kda_noalloc_scratch_bytes",
     "kda_prepare_chunk_indices", "kda_dv_split", "kda_seg_len", "kda_ref_block", "kda_fwd_args_size",
     "kda_stats_size",
     "kda_status_str", "kda_get_stats", "kda_reset_stats", "kda_profile_enable", "kda_profile_read",

@@ -344,6 +344,8 @@ struct kda_ctx {
   std::vector<Release> releases;  // in release order
   std::vector<void*> ev_pool, cev_pool;  // idle plain and completion events
   std::vector<int32_t> bounds_tmp;       // bounds read back from the device
+  void* scratch = nullptr;  // this device's fixed workspace for allocation-free calls (null: none)
+  size_t scratch_bytes = 0;
   uint64_t tick = 0;
   kda_stats stats{};
 };
@@ -779,7 +781,14 @@ kda_status kda_ctx_create(int device, kda_ctx** out) {
   hipDeviceProp_t prop;
   if (hipGetDeviceProperties(&prop, device) != hipSuccess) return KDA_ERR_HIP;
   if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return KDA_ERR_UNSUPPORTED;
-  return kda_ctx_create_with_runtime(&kHipRuntime, prop.multiProcessorCount, out);
+  void* scratch = nullptr;
+  if (kda::scratch_address(device, &scratch)) return KDA_ERR_HIP;
+  kda_status st = kda_ctx_create_with_runtime(&kHipRuntime, prop.multiProcessorCount, out);
+  if (st == KDA_OK) {
+    (*out)->scratch = scratch;
+    (*out)->scratch_bytes = kda::kScratchBytes;
+  }
+  return st;
 }
 
 void kda_ctx_destroy(kda_ctx* ctx) {
@@ -983,6 +992,14 @@ extern "C" {
 kda_status kda_chunk_fwd(kda_ctx* ctx, const kda_fwd_args* a, void* ws, size_t ws_bytes, void* stream) {
   return chunk_fwd_impl(ctx, a, ws, ws_bytes, stream, false);
 }
+
+kda_status kda_chunk_fwd_noalloc(kda_ctx* ctx, const kda_fwd_args* a, void* stream) {
+  if (!ctx) return KDA_ERR_INVALID_ARG;
+  if (!ctx->scratch) return KDA_ERR_UNSUPPORTED;  // a context without a device (test runtime)
+  return chunk_fwd_impl(ctx, a, ctx->scratch, ctx->scratch_bytes, stream, true);
+}
+
+size_t kda_noalloc_scratch_bytes(void) { return kda::kScratchBytes; }
 
 kda_status kda_profile_enable(kda_ctx* ctx, int enable) {
   if (!ctx) return KDA_ERR_INVALID_ARG;

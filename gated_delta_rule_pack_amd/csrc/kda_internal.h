@@ -87,6 +87,14 @@ struct Plan {
   int cu_count;         // compute units of the device (persistent grid sizing)
 };
 
+// Fixed device workspace of the allocation-free call (kda_noalloc.hip): 64 MiB per device,
+// enough for the records of one 4096-token call with 12 heads (54.3 MB) and for any call
+// that takes the decode kernel (which needs none).
+constexpr size_t kScratchBytes = size_t(64) << 20;
+// Device address of that device's copy of the workspace, resolved once per device with the
+// device current (0 on success, else a HIP error code).
+int scratch_address(int device, void** ptr);
+
 // Launchers (defined in the .hip files). Return 0 on success, nonzero HIP error code.
 // start / stop, when not null, are HIP events the launch itself records when the kernel
 // starts and when it completes (no separate marker in the stream). Each launcher is

@@ -237,6 +237,25 @@ kda_status kda_chunk_fwd_validate(const kda_fwd_args* args);
 kda_status kda_chunk_fwd(kda_ctx* ctx, const kda_fwd_args* args, void* workspace,
                          size_t workspace_bytes, void* stream);
 
+/* Allocation-free forward call, for callers that cannot allocate memory around a call
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Same arguments, checks and results as kda_chunk_fwd, with no workspace argument: the
+ * workspace is a fixed array of kda_noalloc_scratch_bytes() bytes (64 MiB) that the
+ * library's code object holds on every device it runs on until the process ends. The
+ * call allocates and frees nothing (no hipMalloc, hipHostMalloc or frees; the metadata
+ * arenas do not grow): when the call's exact workspace (35 328 bytes per chunk and head,
+ * plus segment maps and start states for a segmented call; none for a decode call)
+ * exceeds the array, or its metadata does not fit the arenas' free ranges even after
+ * waiting for the ranges still being read (a counted blocking wait), it returns
+ * KDA_ERR_NO_SPACE before enqueuing anything. 1 x 4096 tokens at H = 12 needs 54.3 MB.
+ * The caller passes every input and output (out, final_state) as for kda_chunk_fwd.
+ * Every call on a GPU uses that GPU's one array, which keeps the last call's contents:
+ * calls that overlap in time on one GPU (other streams, other contexts, other threads)
+ * race on it and must be ordered by the caller. KDA_ERR_UNSUPPORTED on a context made
+ * with kda_ctx_create_with_runtime (it has no device array). */
+kda_status kda_chunk_fwd_noalloc(kda_ctx* ctx, const kda_fwd_args* args, void* stream);
+size_t kda_noalloc_scratch_bytes(void);
+
 /* Host-only chunk table (aiter PR 6912, Changes and Tests): for host bounds
  * cu_host[0..n_seqs], writes pairs (sequence, chunk-within-sequence) of every chunk of
  * `chunk` tokens, sequences in cu order, an empty sequence contributing none.

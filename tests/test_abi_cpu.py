@@ -697,3 +697,14 @@ def test_validation_rejects_record_walk_beyond_32_bits(lib):
         a.cu_seqlens_host = cu.ctypes.data
         assert lib.kda_seg_len(1, 1, -(-T // 32), 0) > 0
         assert lib.kda_chunk_fwd_validate(ctypes.byref(a)) == want, T
+
+
+def test_noalloc_entry_point_needs_a_device_context(lib, fake):
+    """The allocation-free call uses the device's fixed array, which a context made on a
+    stand-in runtime does not have: refused before any work."""
+    bufs = FakeBufs()
+    a, _, _ = _valid_args(bufs, T=100, N=3)
+    assert lib.kda_chunk_fwd_noalloc(fake.ctx, ctypes.byref(a), 0x10) == _lib.KDA_ERR_UNSUPPORTED
+    assert lib.kda_chunk_fwd_noalloc(None, ctypes.byref(a), 0x10) == _lib.KDA_ERR_INVALID_ARG
+    assert fake.log == [] and fake.launches == []
+    assert lib.kda_noalloc_scratch_bytes() == 64 << 20
