@@ -5,7 +5,9 @@ One step = one ``kda_chunk_fwd`` call (metadata lookup, prep kernel, scan kernel
 decode kernel alone when no sequence has more than one token) over one batch of
 synthetic input already resident in HBM. The default workload is the
 1 x 4096-token, 12-head call with a paged fp32 state pool (the per-GPU Kimi-K3 serving
-shape); ``--workload`` selects the other shapes.
+shape); ``--workload`` selects the other shapes. The default run also times the
+1 x 16384-token call and both shapes with every call building and uploading its
+metadata, each with its own roofline, under ``extra_workloads``.
 
 Prints ONE JSON line with the throughput (tokens/s) and per-call latency of the K timed
 calls, the roofline of the dominant kernel and the fp64 oracle timed on the host cores.
@@ -31,6 +33,9 @@ METRIC = "KDA prefill µs/call + tokens/s, H=12 1×4K/1×16K; % of MFMA/HBM peak
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 RECORD_BYTES = 35328  # per (head, chunk) workspace record written by prep, read by scan
+
+HEADLINE = "paged_1x4096_H12"
+EXTRA_16K = "paged_1x16384_H12_pad"
 
 WORKLOADS = {
     "paged_1x4096_H12": "1x4096 tokens, H=12, K=V=128, paged fp32 state pool [64,12,128,128]",
@@ -86,7 +91,10 @@ def cpu_baseline(wl, max_tokens: int, workers: int, min_seconds: float):
             S = dict(initial_state=to_f64(wl.initial_state[:take, h:h + 1]))
         tasks.append((q[:, hq:hq + 1], k[:, hq:hq + 1], v[:, h:h + 1], g[:, h:h + 1], b[:, h:h + 1], cu_s,
                       wl.scale, wl.lower_bound, S))
-    workers = max(1, min(workers, len(tasks)))
+    workers = max(1, workers)
+    # One head per task; with more workers than heads the heads repeat, so that every
+    # worker has one task per pass and all of them run at once.
+    run = [tasks[i % len(tasks)] for i in range(max(workers, len(tasks)))]
     with threadpool_limits(1):
         ctx = mp.get_context("fork")
         with ctx.Pool(workers) as pool:
@@ -94,7 +102,7 @@ def cpu_baseline(wl, max_tokens: int, workers: int, min_seconds: float):
             reps = 0
             t0 = time.perf_counter()
             while True:
-                pool.map(_oracle_head, tasks, chunksize=1)
+                pool.map(_oracle_head, run, chunksize=1)
                 reps += 1
                 wall = time.perf_counter() - t0
                 if wall >= min_seconds:
@@ -117,9 +125,10 @@ def cpu_baseline(wl, max_tokens: int, workers: int, min_seconds: float):
     except OSError:
         pass
     return {
-        "value": reps * tokens / wall, "unit": "tokens/s", "cores": workers, "kind": "oracle",
-        "sample": f"first {tokens} tokens ({take} sequence(s)) of the workload, all {wl.H} heads, "
-                  f"one head per worker process, fp64 numpy token loop, {reps} pass(es)",
+        "value": reps * tokens * len(run) / (wall * wl.H), "unit": "tokens/s", "cores": workers, "kind": "oracle",
+        "sample": f"first {tokens} tokens ({take} sequence(s)) of the workload, {len(run)} head tasks per pass "
+                  f"(the {wl.H} heads, repeated to give each of {workers} worker processes one), fp64 numpy "
+                  f"token loop, {reps} pass(es); tokens/s counts {wl.H} head-tasks as one token",
         "seconds": wall,
         "value_1core": reps1 * tokens / (wall1 * wl.H), "cpu_model": model, "nproc": os.cpu_count(),
     }
@@ -148,16 +157,26 @@ def traffic_from_profiles(kernel: str, workload: str):
     return float(m_bytes.group(1))
 
 
-def algorithmic_bytes(wl, kernel: str, n_chunks: int):
-    """Per-launch algorithmic bytes of one kernel (per-unit figures stated in the design notes).
+KERNEL_BYTES_BASIS = {
+    "prep": "reads q, k, v, raw gate and raw beta per valid token-head; writes one 35328-byte record per chunk-head",
+    "scan": "reads one 35328-byte prep record per chunk-head; writes 256 B of output per token-head; reads "
+            "(flagged) and writes one V x K state per sequence-head (segment maps and start states of a "
+            "segmented call not counted)",
+    "decode": "the method's own bytes: q, k, v, raw gate, raw beta and out per token-head, state read and write",
+}
+
+
+def kernel_bytes(wl, kernel: str, n_chunks: int):
+    """Per-launch bytes one kernel must move in this design (per-unit figures stated in the
+    design notes), or the method's own bytes for ``call``.
 
     prep: reads q, k, v (3 x 256 B), raw gate (512 B fp32 / 256 B bf16) and raw beta
           (4 / 2 B) per valid token-head; writes one 35328-byte record per chunk-head.
     scan: reads each chunk-head record once; writes 256 B of output per token-head;
           reads (when the flag is set) and writes one V x K state per sequence-head.
     decode: the one-token kernel moves exactly the method's own bytes (as ``call``).
-    call: the method's own bytes: q, k, v, raw gate, raw beta, out per token-head plus the
-          state read/write, no intermediates.
+    call: the method's own (algorithmic) bytes: q, k, v, raw gate, raw beta, out per
+          token-head plus the state read/write, no intermediates.
     """
     th = wl.T * wl.H
     qk_b = 2 * 256 * wl.H_qk // wl.H  # q and k bytes per token-head (grouped heads share them)
@@ -243,55 +262,37 @@ def copy_calibration(mib: int, steps: int, warmup: int):
                       "equal": bool(torch.equal(src, dst))}), flush=True)
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__)
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="paged_1x4096_H12")
-    ap.add_argument("--rotate", type=int, default=0,
-                    help="input sets cycled through (0: enough to exceed the 256 MB MALL)")
-    ap.add_argument("--rotate-bounds", type=int, default=0,
-                    help="cycle through this many permutations of the sequence lengths (metadata-cache "
-                         "miss mode: every call uploads its metadata)")
-    ap.add_argument("--cpu-tokens", type=int, default=4096, help="oracle sample size (tokens)")
-    ap.add_argument("--cpu-workers", type=int, default=12)
-    ap.add_argument("--cpu-seconds", type=float, default=2.0, help="minimum oracle wall time")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--copy-mib", type=int, default=0,
-                    help="instead of the workload, run --steps plain device copies of this many MiB "
-                         "(the known-size kernel that scales the HBM byte counters)")
-    args = ap.parse_args()
+def _context_with(env: dict):
+    """A new library context created with these environment knobs set (read once, at creation)."""
+    import gated_delta_rule_pack_amd as kda
+    old = {k: os.environ.get(k) for k in env}
+    os.environ.update({k: str(v) for k, v in env.items()})
+    try:
+        return kda.Context(0)
+    finally:
+        for k, v in old.items():
+            if v is None:
+                del os.environ[k]
+            else:
+                os.environ[k] = v
 
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}, WORLD_SIZE {world}); "
-              "the KDA path here is single-GPU: heads and sequences shard without communication, "
-              "so per-GPU throughput is the number to read.", file=sys.stderr)
-        sys.exit(2)
 
-    if args.copy_mib:
-        copy_calibration(args.copy_mib, args.steps, args.warmup)
-        return
+def measure(name: str, steps: int, warmup: int, rotate: int = 0, rotate_bounds: int = 0, ctx=None):
+    """Time ``steps`` calls of one workload (inputs resident in HBM, rotated over input sets
+    larger than the 256 MB MALL) and, in a second pass, each kernel's own duration.
 
-    from gated_delta_rule_pack_amd.workloads import standard
-    cfg_desc = WORKLOADS[args.workload]
-    wl = standard(args.workload)
-
-    # Oracle baseline on the host first, before anything initialises the GPU.
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, args.cpu_tokens, args.cpu_workers, args.cpu_seconds)
-
+    Returns the fields of one bench record: throughput, latency, per-kernel times and the
+    roofline of the dominant kernel."""
     import torch
 
     import gated_delta_rule_pack_amd as kda
     from gated_delta_rule_pack_amd import _lib
+    from gated_delta_rule_pack_amd.workloads import standard
 
+    wl = standard(name)
     dev = torch.device("cuda", 0)
-    torch.cuda.set_device(dev)
     lib = _lib.load()
-    ctx = kda.get_context(dev)
+    ctx = ctx if ctx is not None else kda.get_context(dev)
     stream = torch.cuda.current_stream(dev)
 
     # Input sets resident in HBM, rotated so the caches cannot hold them between steps.
@@ -300,7 +301,7 @@ def main():
     s_elem = {"f32": 4, "f16": 2, "bf16": 2}[wl.state_dtype]
     per_set = sum(t.numel() * t.element_size() for t in (wl.q, wl.k, wl.v, wl.g_raw, wl.beta_raw)) + \
         wl.v.numel() * 2 + (2 * wl.N * wl.H * 128 * 128 * s_elem if wl.state_mode == "paged" else 0)
-    n_rot = args.rotate or max(1, min(8, (512 << 20) // per_set + 1))
+    n_rot = rotate or max(1, min(8, (512 << 20) // per_set + 1))
     base = {n: getattr(wl, n).to(dev) for n in ("q", "k", "v", "g_raw", "beta_raw")}
     cu_d = wl.cu_seqlens.to(dev)
     cu_h = wl.cu_seqlens.clone()
@@ -313,14 +314,14 @@ def main():
             pools.append(dict(state_cache=storage.as_strided((wl.num_slots, wl.H, 128, 128),
                                                              (wl.state_stride0, 128 * 128, 128, 1)),
                               state_indices=idx_d, has_initial_state=flag_d))
-    # Bounds sets: the workload's own, or (--rotate-bounds K) K seeded permutations of its
+    # Bounds sets: the workload's own, or (rotate_bounds K) K seeded permutations of its
     # sequence lengths, so that every call misses the metadata cache (64 entries).
     bounds = [(cu_d, cu_h)]
-    if args.rotate_bounds:
+    if rotate_bounds:
         gen = torch.Generator().manual_seed(7)
         lens = wl.cu_seqlens[1:] - wl.cu_seqlens[:-1]
         bounds = []
-        for _ in range(args.rotate_bounds):
+        for _ in range(rotate_bounds):
             perm = lens[torch.randperm(wl.N, generator=gen)]
             h_cu = torch.cat([torch.zeros(1, dtype=torch.int32), torch.cumsum(perm, 0).to(torch.int32)])
             bounds.append((h_cu.to(dev), h_cu))
@@ -343,14 +344,14 @@ def main():
     n_rot = len(sets)
     ws_bytes = kda.workspace_bytes(sets[0][1])
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-    ws_p, ws_n, st_p = ctypes.c_void_p(ws.data_ptr()), ctypes.c_size_t(ws_bytes), ctypes.c_void_p(stream.cuda_stream)
+    ws_p, st_p = ws.data_ptr(), stream.cuda_stream
 
     def step(i):
-        rc = lib.kda_chunk_fwd(ctx.ptr, ctypes.byref(sets[i % n_rot][1]), ws_p, ws_n, st_p)
+        rc = ctx.forward(sets[i % n_rot][1], ws_p, ws_bytes, st_p)
         if rc != _lib.KDA_OK:
             raise kda.KDAError(rc, "kda_chunk_fwd")
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
     ctx.reset_stats()
@@ -360,7 +361,7 @@ def main():
     torch.cuda.synchronize()
     e0.record(stream)
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         step(i)
     e1.record(stream)
     torch.cuda.synchronize()
@@ -369,17 +370,15 @@ def main():
     # Kernel durations: the same K calls again, with the library's timing events attached
     # to each kernel launch (start and end of the kernel itself, on the call stream).
     ctx.profile(True)
-    for i in range(args.steps):
+    for i in range(steps):
         step(i)
     torch.cuda.synchronize()
     ctx.profile(False)
-    per_call = sorted(ctx.profile_calls(args.steps))
+    per_call = sorted(ctx.profile_calls(steps))
     prep_ms, scan_ms, ncalls = ctx.profile_read()
     pct = lambda f: 1e3 * per_call[min(len(per_call) - 1, int(f * len(per_call)))]
-    ms_total = e0.elapsed_time(e1)
-    ms_step = ms_total / args.steps
-    tokens = wl.T
-    value = tokens / (ms_step * 1e-3)
+    ms_step = e0.elapsed_time(e1) / steps
+    value = wl.T / (ms_step * 1e-3)
 
     n_chunks = int(stats["last_n_chunks"])
     if stats["last_path"] == 1:  # one-token call: the decode kernel alone
@@ -387,47 +386,124 @@ def main():
     else:
         k_us = {"prep": 1e3 * prep_ms / max(ncalls, 1), "scan": 1e3 * scan_ms / max(ncalls, 1)}
     dom = max(k_us, key=k_us.get)
-    ab = algorithmic_bytes(wl, dom, n_chunks)
-    achieved = ab / (k_us[dom] * 1e-6) / 1e9
-    traffic = traffic_from_profiles(dom, args.workload)
-    call_bytes = algorithmic_bytes(wl, "call", n_chunks)
+    kb = kernel_bytes(wl, dom, n_chunks)
+    achieved = kb / (k_us[dom] * 1e-6) / 1e9
+    traffic = traffic_from_profiles(dom, name)
+    call_bytes = kernel_bytes(wl, "call", n_chunks)
     flops = algorithmic_flops(wl, dom)
     call_flops = algorithmic_flops(wl, "decode" if dom == "decode" else "call")
+    segmented = dom == "scan" and stats["last_seg_len"] > 0
     roofline = {
         "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
         "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-        "kernel": f"kda_{dom}" + (" phase: segment maps, segment combine, scan"
-                                   if dom == "scan" and stats["last_seg_len"] > 0 else ""),
-        "kernel_us": round(k_us[dom], 2), "algorithmic_bytes": int(ab),
+        "kernel": f"kda_{dom}" + (" phase: segment maps, segment combine, scan" if segmented else ""),
+        "kernel_us": round(k_us[dom], 2),
+        # The bytes this kernel must move in the two-kernel design (the per-kernel accounting:
+        # for the scan, the prep records it reads, its output and the state), which is what
+        # `achieved` and `frac` use.
+        "kernel_bytes": int(kb),
+        "kernel_bytes_basis": KERNEL_BYTES_BASIS[dom],
+        # The method's own bytes (q, k, v, raw gate, raw beta and out per token-head plus the
+        # state read and write, no intermediates), against the whole call's time.
         "call_algorithmic_bytes": int(call_bytes),
         "call_frac": round(call_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "kernel_tflops": round(flops / (k_us[dom] * 1e-6) / 1e12, 2),
         "kernel_mfma_frac": round(flops / (k_us[dom] * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
         "call_tflops": round(call_flops / (ms_step * 1e-3) / 1e12, 2),
         "call_mfma_frac": round(call_flops / (ms_step * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-        "attainable": attainable_peaks(dev),
     }
-    line = {
-        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
-        "us_per_call": round(ms_step * 1e3, 2), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": args.workload, "description": cfg_desc, "T": wl.T, "N": wl.N, "H": wl.H,
-                   "H_qk": wl.H_qk, "K": 128, "V": 128, "chunk": 32, "state_k_first": wl.state_k_first,
-                   "lower_bound": wl.lower_bound, "state": f"{wl.state_mode} {wl.state_dtype}",
-                   "dv_split": stats["last_dv_split"], "ref_block": stats["last_ref_block"],
-                   "input_sets_rotated": n_rot, "bounds_sets": max(1, args.rotate_bounds),
-                   "parallelism": "single GPU"},
+    config = {"workload": name, "description": WORKLOADS[name], "T": wl.T, "N": wl.N, "H": wl.H,
+              "H_qk": wl.H_qk, "K": 128, "V": 128, "chunk": 32, "state_k_first": wl.state_k_first,
+              "lower_bound": wl.lower_bound, "state": f"{wl.state_mode} {wl.state_dtype}",
+              "dv_split": stats["last_dv_split"], "ref_block": stats["last_ref_block"],
+              "segment_length": stats["last_seg_len"], "input_sets_rotated": n_rot,
+              "bounds_sets": max(1, rotate_bounds), "parallelism": "single GPU"}
+    return {
+        "value": round(value, 1), "unit": "tokens/s", "ms_per_step": round(ms_step, 5),
+        "us_per_call": round(ms_step * 1e3, 2), "steps": steps, "warmup": warmup, "config": config,
         "kernels_us": {k: round(v, 2) for k, v in k_us.items()},
         # Per-call latency from the kernels' own timestamps (first kernel start to scan
         # end), over the profiled pass.
         "call_us_p10_p50_p90": [round(pct(0.1), 2), round(pct(0.5), 2), round(pct(0.9), 2)],
-        "host_wall_us_per_call": round(wall / args.steps * 1e6, 2),
+        "host_wall_us_per_call": round(wall / steps * 1e6, 2),
         "metadata": {"cache_hits": stats["cache_hits"], "cache_misses": stats["cache_misses"],
-                     "blocking_syncs": stats["blocking_syncs"]},
+                     "blocking_syncs": stats["blocking_syncs"], "arena_grows": stats["arena_grows"]},
         "roofline": roofline,
-        "cpu_baseline": cpu,
     }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", choices=sorted(WORKLOADS), default=HEADLINE)
+    ap.add_argument("--rotate", type=int, default=0,
+                    help="input sets cycled through (0: enough to exceed the 256 MB MALL)")
+    ap.add_argument("--rotate-bounds", type=int, default=0,
+                    help="cycle through this many permutations of the sequence lengths (metadata-cache "
+                         "miss mode: every call uploads its metadata)")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="time only --workload (by default the headline run also times the 1x16384 shape, "
+                         "and both headline shapes with every call missing the metadata cache)")
+    ap.add_argument("--cpu-tokens", type=int, default=4096, help="oracle sample size (tokens)")
+    ap.add_argument("--cpu-workers", type=int, default=0, help="oracle worker processes (0: all host cores, at most 16)")
+    ap.add_argument("--cpu-seconds", type=float, default=2.0, help="minimum oracle wall time")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="instead of the workload, run --steps plain device copies of this many MiB "
+                         "(the known-size kernel that scales the HBM byte counters)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the KDA path here is single-GPU: heads and sequences shard without communication, "
+              "so per-GPU throughput is the number to read.", file=sys.stderr)
+        sys.exit(2)
+
+    if args.copy_mib:
+        copy_calibration(args.copy_mib, args.steps, args.warmup)
+        return
+
+    from gated_delta_rule_pack_amd.workloads import standard
+
+    # Oracle baseline on the host first, before anything initialises the GPU.
+    cpu = None
+    if not args.no_cpu_baseline:
+        workers = args.cpu_workers or min(16, os.cpu_count() or 1)
+        cpu = cpu_baseline(standard(args.workload), args.cpu_tokens, workers, args.cpu_seconds)
+
+    import torch
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    rec = measure(args.workload, args.steps, args.warmup, args.rotate, args.rotate_bounds)
+    rec["roofline"]["attainable"] = attainable_peaks(dev)
+    extra = None
+    if args.workload == HEADLINE and not args.no_extra and not args.rotate_bounds:
+        # The second headline shape, and both shapes with every call building and uploading
+        # its metadata (a context whose metadata cache is off, as with new bounds each call).
+        extra = {}
+        for key, name, env in ((EXTRA_16K, EXTRA_16K, None), (HEADLINE + "_meta_miss", HEADLINE, {"KDA_META_CACHE": 0}),
+                               (EXTRA_16K + "_meta_miss", EXTRA_16K, {"KDA_META_CACHE": 0})):
+            ctx = _context_with(env) if env else None
+            extra[key] = measure(name, args.steps, args.warmup, args.rotate, ctx=ctx)
+            if env:
+                extra[key]["config"]["metadata"] = "every call builds and uploads its metadata (KDA_META_CACHE=0)"
+                ctx.close()
+    line = {
+        "metric": METRIC, "value": rec["value"], "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": rec["ms_per_step"],
+        "us_per_call": rec["us_per_call"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": rec["config"], "kernels_us": rec["kernels_us"],
+        "call_us_p10_p50_p90": rec["call_us_p10_p50_p90"], "host_wall_us_per_call": rec["host_wall_us_per_call"],
+        "metadata": rec["metadata"], "roofline": rec["roofline"], "cpu_baseline": cpu,
+    }
+    if extra is not None:
+        line["extra_workloads"] = {
+            k: {f: v[f] for f in ("value", "unit", "us_per_call", "ms_per_step", "kernels_us", "call_us_p10_p50_p90",
+                                  "metadata", "roofline", "config")} for k, v in extra.items()}
     print(json.dumps(line), flush=True)
 
 

@@ -335,6 +335,8 @@ struct kda_ctx {
   int dv_split_override = 0;  // tuning only (KDA_DV_SPLIT), 0 = policy
   int seg_len_override = -1;  // tuning only (KDA_SEG_LEN), -1 = policy, 0 = never segment
   bool decode_off = false;    // testing only (KDA_DECODE=0): one-token calls take the chunked path
+  bool cache_off = false;     // measurement only (KDA_META_CACHE=0): every call builds and uploads
+                              // its metadata, as a call with new bounds does
   bool profiling = false;
   std::vector<ProfileMarks> marks;       // recorded, not yet read
   std::vector<ProfileMarks> marks_free;  // reusable
@@ -540,6 +542,7 @@ kda_status get_meta(kda_ctx* ctx, const int32_t* cu, int N, int seg_len, void* s
   if (ctx->rt.stream_is_capturing(ctx->rt.user, stream, &capturing)) return hip_fail();
   const uint64_t hsh = hash_bounds(cu, N);
   for (CacheEntry* e : ctx->cache) {
+    if (ctx->cache_off && !capturing) break;
     if (e->hash == hsh && e->seg_len == seg_len && (int)e->bounds.size() == N + 1 &&
         std::memcmp(e->bounds.data(), cu, (N + 1) * sizeof(int32_t)) == 0) {
       // A hit from another stream waits for the upload. Under capture the wait would
@@ -762,6 +765,7 @@ kda_status kda_ctx_create_with_runtime(const kda_runtime* rt, int cu_count, kda_
     if (v == 1 || v == 2 || v == 4 || v == 8) ctx->dv_split_override = v;
   }
   if (const char* e = std::getenv("KDA_DECODE")) ctx->decode_off = e[0] == '0';
+  if (const char* e = std::getenv("KDA_META_CACHE")) ctx->cache_off = e[0] == '0';
   if (const char* e = std::getenv("KDA_SEG_LEN")) {
     const int v = std::atoi(e);
     if (v == 0 || v >= kda::kSegMin) ctx->seg_len_override = v;

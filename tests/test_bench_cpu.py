@@ -19,8 +19,8 @@ def test_decode_bytes_are_tokens_plus_state():
     # 256 B of output; every sequence-head reads and writes a 128 x 128 bf16 state.
     tokens = 256 * 12 * (3 * 256 + 512 + 4 + 256)
     state = 2 * 256 * 12 * 128 * 128 * 2
-    assert bench.algorithmic_bytes(wl, "decode", 256) == tokens + state == 206_057_472
-    assert bench.algorithmic_bytes(wl, "call", 256) == tokens + state
+    assert bench.kernel_bytes(wl, "decode", 256) == tokens + state == 206_057_472
+    assert bench.kernel_bytes(wl, "call", 256) == tokens + state
 
 
 def test_4k_call_flops():
@@ -35,7 +35,7 @@ def test_scan_bytes_count_records_output_and_state():
     wl = standard("paged_1x4096_H12")
     n_chunks = 128
     want = n_chunks * 12 * bench.RECORD_BYTES + 4096 * 12 * 256 + 2 * 12 * 128 * 128 * 4
-    assert bench.algorithmic_bytes(wl, "scan", n_chunks) == want
+    assert bench.kernel_bytes(wl, "scan", n_chunks) == want
 
 
 @pytest.mark.parametrize("gpus", ["2", "8"])
@@ -53,5 +53,5 @@ def test_grouped_heads_read_fewer_qk_bytes():
     f = standard("paged_1x4096_H12")
     assert g.H == f.H == 12 and g.H_qk == 6
     th = 4096 * 12
-    assert bench.algorithmic_bytes(f, "call", 128) - bench.algorithmic_bytes(g, "call", 128) == th * 256
-    assert bench.algorithmic_bytes(f, "scan", 128) == bench.algorithmic_bytes(g, "scan", 128)
+    assert bench.kernel_bytes(f, "call", 128) - bench.kernel_bytes(g, "call", 128) == th * 256
+    assert bench.kernel_bytes(f, "scan", 128) == bench.kernel_bytes(g, "scan", 128)
