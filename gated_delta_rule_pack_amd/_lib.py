@@ -78,6 +78,7 @@ ALLOC = CFUNCTYPE(c_int, c_void_p, POINTER(c_void_p), c_size_t)
 FREE = CFUNCTYPE(c_int, c_void_p, c_void_p)
 LAUNCH = CFUNCTYPE(c_int, c_void_p, c_int, c_void_p, c_void_p, c_void_p, c_void_p)
 ELAPSED = CFUNCTYPE(c_int, c_void_p, POINTER(c_float), c_void_p, c_void_p)
+UPLOAD = CFUNCTYPE(c_int, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p, c_void_p)
 
 
 class Runtime(Structure):
@@ -92,6 +93,7 @@ class Runtime(Structure):
         ("launch", LAUNCH),
         ("event_create_timed", EVCREATE), ("event_elapsed_ms", ELAPSED),
         ("event_create_completion", EVCREATE),
+        ("upload", UPLOAD),
     ]
 
 

@@ -19,7 +19,7 @@ BUILD_DIR = os.path.join(PKG, "_build")
 LIB_NAME = "libkda.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
-SOURCES = ["kda_host.cpp", "kda_prep.hip", "kda_scan.hip", "kda_seg.hip", "kda_decode.hip", "kda_noalloc.hip"]
+SOURCES = ["kda_host.cpp", "kda_prep.hip", "kda_scan.hip", "kda_seg.hip", "kda_decode.hip", "kda_noalloc.hip", "kda_meta.hip"]
 ARCH = "gfx950"
 # Packed fp32 instructions are disabled for every HIP translation unit.
 COMMON_FLAGS = [

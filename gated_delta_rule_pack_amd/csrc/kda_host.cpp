@@ -31,8 +31,11 @@ using kda::kHead;
 namespace {
 
 // ------------------------------------------------------------------ real HIP runtime
-int rt_h2d(void*, void* dst, const void* src, size_t n, void* s) {
-  return (int)hipMemcpyAsync(dst, src, n, hipMemcpyHostToDevice, (hipStream_t)s);
+// The only host-to-device copies are metadata uploads from the pinned staging arena
+// (16-byte aligned, multiples of 16 bytes): a copy kernel on the stream reads them.
+int rt_h2d(void*, void* dst, const void* src, size_t n, void* s) { return kda::launch_meta_copy(src, dst, n, s, nullptr); }
+int rt_upload(void*, void* dst, const void* src, size_t n, void* s, void* done) {
+  return kda::launch_meta_copy(src, dst, n, s, done);
 }
 int rt_d2h(void*, void* dst, const void* src, size_t n, void* s) {
   return (int)hipMemcpyAsync(dst, src, n, hipMemcpyDeviceToHost, (hipStream_t)s);
@@ -87,7 +90,8 @@ int rt_ev_elapsed(void*, float* ms, void* a, void* b) {
 const kda_runtime kHipRuntime = {nullptr,    rt_h2d,        rt_d2h,         rt_sync,     rt_capturing,
                                  rt_ev_create, rt_ev_destroy, rt_ev_record, rt_ev_query, rt_ev_sync,
                                  rt_wait,    rt_host_alloc, rt_host_free,   rt_dev_alloc, rt_dev_free,
-                                 rt_launch,  rt_ev_create_timed, rt_ev_elapsed, rt_ev_create_completion};
+                                 rt_launch,  rt_ev_create_timed, rt_ev_elapsed, rt_ev_create_completion,
+                                 rt_upload};
 
 // ------------------------------------------------------------------ metadata
 inline size_t align4(size_t n) { return (n + 3) & ~size_t(3); }  // int32 count -> 16-byte blocks
@@ -307,6 +311,9 @@ struct Release {
   Arena* arena = nullptr;
   void* ptr = nullptr;
   size_t bytes = 0;
+  Arena* arena2 = nullptr;  // a second range released with the first (null: none)
+  void* ptr2 = nullptr;
+  size_t bytes2 = 0;
   std::vector<void*> events;       // plain events, back to their pool afterwards
   std::vector<void*> completions;  // launch-attached completion events, back to their pool
 };
@@ -316,6 +323,8 @@ struct CacheEntry {
   int seg_len = 0;
   uint64_t hash = 0;
   void* dev = nullptr;          // device metadata buffer (a range of the device arena)
+  void* stage = nullptr;        // its pinned staging copy (a range of the pinned arena), kept
+                                // with the entry, so that no event of its own tracks the upload
   size_t bytes = 0;
   Meta meta;
   void* upload_event = nullptr;  // recorded right after the upload
@@ -436,6 +445,7 @@ bool release_done(kda_ctx* ctx, const Release& r) {
 
 void finish_release(kda_ctx* ctx, Release& r) {
   arena_give(*r.arena, r.ptr, r.bytes);
+  if (r.arena2) arena_give(*r.arena2, r.ptr2, r.bytes2);
   ctx->ev_pool.insert(ctx->ev_pool.end(), r.events.begin(), r.events.end());
   ctx->cev_pool.insert(ctx->cev_pool.end(), r.completions.begin(), r.completions.end());
 }
@@ -455,13 +465,13 @@ void sweep(kda_ctx* ctx) {
   rs.resize(w);
 }
 
-// Allocation-free calls only: wait for the oldest pending release of arena a (one counted
-// blocking wait) and take it back. *waited is false when none is pending.
+// Allocation-free calls only: wait for the oldest pending release that returns a range of
+// arena a (one counted blocking wait) and take it back. *waited is false when none is pending.
 kda_status wait_oldest(kda_ctx* ctx, Arena& a, bool* waited) {
   *waited = false;
   auto& rs = ctx->releases;
   for (size_t i = 0; i < rs.size(); ++i) {
-    if (rs[i].arena != &a) continue;
+    if (rs[i].arena != &a && rs[i].arena2 != &a) continue;
     for (void* e : rs[i].events)
       if (ctx->rt.event_synchronize(ctx->rt.user, e)) return hip_fail();
     for (void* e : rs[i].completions)
@@ -479,7 +489,8 @@ bool evict_one(kda_ctx* ctx);
 
 // A range of `bytes` from arena a. may_grow: add a block when nothing fits (never waits).
 // Otherwise (allocation-free calls) wait for pending releases, evicting cached metadata
-// when the device arena is full of it; KDA_ERR_NO_SPACE when the request cannot fit.
+// (whose device buffer and staging copy hold both arenas) when they are full of it;
+// KDA_ERR_NO_SPACE when the request cannot fit.
 kda_status arena_alloc(kda_ctx* ctx, Arena& a, size_t bytes, bool may_grow, void** out) {
   for (;;) {
     if ((*out = arena_take(a, bytes))) return KDA_OK;
@@ -493,7 +504,7 @@ kda_status arena_alloc(kda_ctx* ctx, Arena& a, size_t bytes, bool may_grow, void
     bool waited = false;
     if (kda_status st = wait_oldest(ctx, a, &waited)) return st;
     if (waited) continue;
-    if (&a == &ctx->dev_arena && evict_one(ctx)) continue;
+    if (evict_one(ctx)) continue;  // an entry's device buffer and staging copy come back together
     return KDA_ERR_NO_SPACE;
   }
 }
@@ -512,6 +523,9 @@ bool evict_one(kda_ctx* ctx) {
   r.arena = &ctx->dev_arena;
   r.ptr = e->dev;
   r.bytes = e->bytes;
+  r.arena2 = &ctx->host_arena;
+  r.ptr2 = e->stage;
+  r.bytes2 = e->bytes;
   if (e->upload_event) r.events.push_back(e->upload_event);
   for (auto& u : e->uses) r.completions.push_back(u.second);
   ctx->releases.push_back(std::move(r));
@@ -587,24 +601,25 @@ kda_status get_meta(kda_ctx* ctx, const int32_t* cu, int N, int seg_len, void* s
   e->hash = hsh;
   e->meta = m;
   e->bytes = bytes;
-  void* stage_ev = nullptr;
-  if (ev_get(ctx, false, &e->upload_event) || ev_get(ctx, false, &stage_ev) ||
-      ctx->rt.memcpy_h2d_async(ctx->rt.user, e->dev, stage, bytes, stream) ||
-      ctx->rt.event_record(ctx->rt.user, e->upload_event, stream) ||
-      ctx->rt.event_record(ctx->rt.user, stage_ev, stream)) {
+  e->stage = stage;
+  // One upload whose completion the copy itself records (no marker in the stream); the
+  // staging range stays with the entry and goes back with its device buffer.
+  int rc = ev_get(ctx, false, &e->upload_event) != KDA_OK;
+  if (!rc) {
+    if (ctx->rt.upload) {
+      rc = ctx->rt.upload(ctx->rt.user, e->dev, stage, bytes, stream, e->upload_event);
+    } else {
+      rc = ctx->rt.memcpy_h2d_async(ctx->rt.user, e->dev, stage, bytes, stream) ||
+           ctx->rt.event_record(ctx->rt.user, e->upload_event, stream);
+    }
+  }
+  if (rc) {
     // Nothing reads the ranges if the copy was not enqueued; if it was, they stay held
     // (the copy may still run) until the context is destroyed.
     if (e->upload_event) ctx->ev_pool.push_back(e->upload_event);
-    if (stage_ev) ctx->ev_pool.push_back(stage_ev);
     delete e;
     return hip_fail();
   }
-  Release r;
-  r.arena = &ctx->host_arena;
-  r.ptr = stage;
-  r.bytes = bytes;
-  r.events.push_back(stage_ev);
-  ctx->releases.push_back(std::move(r));
   e->upload_stream = stream;
   e->tick = ++ctx->tick;
   ctx->cache.push_back(e);

@@ -105,5 +105,9 @@ int launch_scan(const Plan& p, void* stream, void* start, void* stop);
 int launch_segmap(const Plan& p, void* stream, void* start, void* stop);
 int launch_segcombine(const Plan& p, void* stream, void* start, void* stop);
 int launch_decode(const Plan& p, void* stream, void* start, void* stop);
+// Copies bytes (a multiple of 16, both pointers 16-byte aligned) from device-readable
+// pinned host memory to device memory with a kernel on the stream.
+// done, when not null, is an event the launch records when the copy has completed.
+int launch_meta_copy(const void* host_src, void* dst, size_t bytes, void* stream, void* done);
 
 }  // namespace kda

@@ -180,6 +180,10 @@ typedef struct kda_runtime {
   /* Completion events: they only tell the host that a launch has finished (they track the
    * last use of a cached metadata buffer) and carry no memory fence. */
   int (*event_create_completion)(void* user, void** event);
+  /* Metadata upload (optional; null means memcpy_h2d_async followed by event_record): copies
+   * bytes from pinned host memory to device memory on stream and records done_event when the
+   * copy has completed, with no separate marker in the stream. */
+  int (*upload)(void* user, void* dst, const void* src, size_t bytes, void* stream, void* done_event);
 } kda_runtime;
 
 /* Context (aiter PR 6912, Changes: metadata built from host bounds, uploaded with one

@@ -258,7 +258,8 @@ class FakeRuntime:
             host_alloc_pinned=_lib.ALLOC(self._halloc), host_free_pinned=_lib.FREE(self._hfree),
             device_alloc=_lib.ALLOC(self._dalloc), device_free=_lib.FREE(self._dfree),
             launch=_lib.LAUNCH(self._launch), event_create_timed=_lib.EVCREATE(self._ev_create),
-            event_elapsed_ms=_lib.ELAPSED(self._elapsed), event_create_completion=_lib.EVCREATE(self._ev_create))
+            event_elapsed_ms=_lib.ELAPSED(self._elapsed), event_create_completion=_lib.EVCREATE(self._ev_create),
+            upload=_lib.UPLOAD(self._upload))
         for k, v in self._cbs.items():
             setattr(rt, k, v)
         self.rt = rt
@@ -267,6 +268,13 @@ class FakeRuntime:
         ctypes.memmove(dst, src, n)
         self.uploads.append((dst, n, s, np.frombuffer(ctypes.string_at(src, n), np.int32).copy()))
         self.log.append(("h2d", s))
+        return 0
+
+    def _upload(self, user, dst, src, n, s, done):
+        # A copy whose completion event the copy records itself (no separate marker).
+        self._h2d(user, dst, src, n, s)
+        self.pending.add(done)
+        self.log.append(("record", done, s))
         return 0
 
     def _d2h(self, user, dst, src, n, s):
@@ -292,6 +300,7 @@ class FakeRuntime:
         return 0
 
     def _ev_record(self, user, e, s):
+        self.marker_records = getattr(self, "marker_records", 0) + 1
         self.pending.add(e)
         self.log.append(("record", e, s))
         return 0
@@ -708,3 +717,16 @@ def test_noalloc_entry_point_needs_a_device_context(lib, fake):
     assert lib.kda_chunk_fwd_noalloc(None, ctypes.byref(a), 0x10) == _lib.KDA_ERR_INVALID_ARG
     assert fake.log == [] and fake.launches == []
     assert lib.kda_noalloc_scratch_bytes() == 64 << 20
+
+
+def test_miss_enqueues_no_separate_event_marker(lib, fake):
+    """A metadata miss enqueues the upload, whose completion the copy records itself, and
+    the launches: no event is recorded as a separate marker in the stream (each marker costs
+    the GPU several microseconds of idle time)."""
+    bufs = FakeBufs()
+    for i in range(3):
+        a, _, _ = _valid_args(bufs, T=300 + i, N=4, cu=np.array([0, 0, 100, 100, 300 + i], np.int32), paged=True)
+        assert _call(lib, fake, a) == _lib.KDA_OK
+    assert getattr(fake, "marker_records", 0) == 0
+    assert [e[0] for e in fake.log].count("h2d") == 3
+    assert _stats(lib, fake)["cache_misses"] == 3
