@@ -162,6 +162,14 @@ __device__ __forceinline__ void* state_out_plane(const Plan& p, int n, int h) {
   return nullptr;
 }
 
+// Position of element (k, k') of a segment map's A^T plane (A^T[k][k'] = A[k'][k]) in the
+// segment combine kernel's MFMA operand fragment order: fragment (k / 16) * 4 + k' / 32 of
+// 64 lanes x 8 bf16, lane (k % 16) + 16 ((k' % 32) / 8), element k' % 8. One fragment is
+// 1 KB of contiguous bytes, which the combine streams into LDS with one direct load.
+__device__ __forceinline__ int map_frag_index(int k, int kp) {
+  return ((k >> 4) * 4 + (kp >> 5)) * 512 + ((k & 15) + 16 * ((kp & 31) >> 3)) * 8 + (kp & 7);
+}
+
 // Barrier for waves that touch LDS only with ds instructions: their LDS writes are
 // complete (lgkmcnt) before it and no LDS read moves above it.
 __device__ __forceinline__ void barrier_lds() {

@@ -41,7 +41,7 @@ constexpr int kSegInts = 8;       // segment table record: sequence, first chunk
                                   // start-state slot (-1: the caller's initial state, read
                                   // only by a sequence's single segment),
                                   // own map slot (-1: last segment, writes the final state)
-constexpr size_t kMapBytes = (size_t)2 * kHead * kHead * 4;  // A (bf16 hi, lo), C (fp32), [k][v] each
+constexpr size_t kMapBytes = (size_t)2 * kHead * kHead * 4;  // A (bf16 hi, lo; [k][k']), C (fp32; [v][k])
 constexpr size_t kStartBytes = (size_t)kHead * kHead * 4;    // start state, fp32, [v][k]
 
 enum StateMode : int { kStateNone = 0, kStateDense = 1, kStatePaged = 2 };
@@ -79,8 +79,8 @@ struct Plan {
   const uint8_t* flags;
   void* out;
   void* ws;             // first chunk record (256-byte aligned)
-  float* maps;          // [n_maps][H] segment maps: A as bf16 hi and lo planes, then C fp32,
-                        // each [K][V] (S^T layout)
+  float* maps;          // [n_maps][H] segment maps: A as bf16 hi and lo planes [k][k'] (A^T),
+                        // then C fp32 [v][k]
   float* starts;        // [n_maps + n_multi][H][V][K] fp32 start states: slot m < n_maps
                         // starts the segment after map slot m, slot n_maps + k the first
                         // segment of multi-segment sequence k (its initial state)

@@ -332,32 +332,44 @@ __global__ __launch_bounds__(320, 1) void head_kernel(Plan p, int units, int gro
           store_state4_vk<SDT>(out_plane, 16 * (vt0 + nt) + l16, 16 * tt + 4 * g4, S[nt][tt], KF);
     }
   } else {
-    // Map slot layout (kMapBytes): A as bf16 hi and lo planes, then C in fp32, each in
-    // S^T order: element (k, v) at [k][v] (for A, v is the input key k').
+    // Map slot layout (kMapBytes): A^T as bf16 hi and lo planes in the combine kernel's
+    // MFMA operand fragment order (map_frag_index), then C in fp32 in S order (element
+    // (v, k) at [v][k]).
     char* base = reinterpret_cast<char*>(p.maps) + (size_t)(un.m_self * p.H + h) * kMapBytes;
     if (part_a) {
-      __bf16* hi = reinterpret_cast<__bf16*>(base);
-      __bf16* lo = hi + kHead * kHead;
+      // Wave w holds input keys k' = 32w .. 32w + 31 (NTW = 2), i.e. key block w of every
+      // fragment: it transposes them through its own LDS region (the ring is no longer
+      // read once every chunk is done) and writes each fragment row as 16 bytes.
+      static_assert(NTW == 2, "one key block of 32 input keys per wave");
+      constexpr int kLdT = 40;  // bf16 per LDS row: 32 input keys + pad
+      __bf16* th = reinterpret_cast<__bf16*>(lds) + wave * 2 * kHead * kLdT;
+      __bf16* tl = th + kHead * kLdT;
 #pragma unroll
       for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
         for (int tt = 0; tt < 8; ++tt)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const size_t at = (size_t)(16 * tt + 4 * g4 + i) * kHead + 16 * (vt0 + nt) + l16;
-            __bf16 a, b;
-            split_bf16(S[nt][tt][i], a, b);
-            hi[at] = a;
-            lo[at] = b;
+            const int at = (16 * tt + 4 * g4 + i) * kLdT + 16 * nt + l16;
+            split_bf16(S[nt][tt][i], th[at], tl[at]);
           }
+      __bf16* hi = reinterpret_cast<__bf16*>(base);
+      __bf16* lo = hi + kHead * kHead;
+#pragma unroll
+      for (int kt = 0; kt < 8; ++kt) {
+        // Fragment (kt, kb = wave), lane (l16, g4): A^T[16 kt + l16][32 wave + 8 g4 .. + 7].
+        const int src = (16 * kt + l16) * kLdT + 8 * g4;
+        const int dst = map_frag_index(16 * kt + l16, 32 * wave + 8 * g4);
+        *reinterpret_cast<bf16x8*>(hi + dst) = *reinterpret_cast<const bf16x8*>(th + src);
+        *reinterpret_cast<bf16x8*>(lo + dst) = *reinterpret_cast<const bf16x8*>(tl + src);
+      }
     } else {
       float* dst = reinterpret_cast<float*>(base + kHead * kHead * 4);
 #pragma unroll
       for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
         for (int tt = 0; tt < 8; ++tt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) dst[(size_t)(16 * tt + 4 * g4 + i) * kHead + 16 * (vt0 + nt) + l16] = S[nt][tt][i];
+          *reinterpret_cast<f32x4*>(dst + (size_t)(16 * (vt0 + nt) + l16) * kHead + 16 * tt + 4 * g4) = S[nt][tt];
     }
   }
 }
