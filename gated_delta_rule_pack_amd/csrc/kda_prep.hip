@@ -123,14 +123,14 @@ __device__ __forceinline__ void load_inputs(const Plan& p, const Item& it, int w
   for (int i = 0; i < 8; ++i) {
     const int vo = (8 * w + i) * row2 + lane * 4;
     const int vqk = GVA ? (8 * w + i) * Hqk * kHead * 2 + lane * 4 : vo;
-    in.q[i] = __builtin_amdgcn_raw_buffer_load_b32(rq, vqk, 0, 0);
-    in.k[i] = __builtin_amdgcn_raw_buffer_load_b32(rk, vqk, 0, 0);
-    in.v[i] = __builtin_amdgcn_raw_buffer_load_b32(rv, vo, 0, 0);
+    in.q[i] = __builtin_amdgcn_raw_buffer_load_b32(rq, vqk, 0, kStreamLoad);
+    in.k[i] = __builtin_amdgcn_raw_buffer_load_b32(rk, vqk, 0, kStreamLoad);
+    in.v[i] = __builtin_amdgcn_raw_buffer_load_b32(rv, vo, 0, kStreamLoad);
     if constexpr (GF32) {
-      const auto g = __builtin_amdgcn_raw_buffer_load_b64(rg, 2 * vo, 0, 0);
+      const auto g = __builtin_amdgcn_raw_buffer_load_b64(rg, 2 * vo, 0, kStreamLoad);
       in.g[i] = make_float2(__uint_as_float(g[0]), __uint_as_float(g[1]));
     } else {
-      const uint32_t g = __builtin_amdgcn_raw_buffer_load_b32(rg, vo, 0, 0);
+      const uint32_t g = __builtin_amdgcn_raw_buffer_load_b32(rg, vo, 0, kStreamLoad);
       in.g[i] = make_float2(__uint_as_float(g << 16), __uint_as_float(g & 0xffff0000u));
     }
   }
