@@ -960,6 +960,7 @@ kda_status chunk_fwd_impl(kda_ctx* ctx, const kda_fwd_args* a, void* ws, size_t 
   p.maps = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + wl.maps);
   p.starts = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + wl.starts);
   p.cu_count = ctx->cu_count;
+  p.stream_inputs = (size_t)a->H * (size_t)p.n_chunks * kda::kRecBytes <= kda::kMallBytes;
 
   // Launches. Under capture the entry is retained (never evicted), so no completion event
   // is attached, and no timing events are recorded.

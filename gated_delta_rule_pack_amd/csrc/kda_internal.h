@@ -85,12 +85,17 @@ struct Plan {
                         // starts the segment after map slot m, slot n_maps + k the first
                         // segment of multi-segment sequence k (its initial state)
   int cu_count;         // compute units of the device (persistent grid sizing)
+  int stream_inputs;    // prep reads its inputs with the non-temporal hint (the call's chunk
+                        // records fit the memory-side cache)
 };
 
 // Fixed device workspace of the allocation-free call (kda_noalloc.hip): 64 MiB per device,
 // enough for the records of one 4096-token call with 12 heads (54.3 MB) and for any call
 // that takes the decode kernel (which needs none).
 constexpr size_t kScratchBytes = size_t(64) << 20;
+// Memory-side cache of an MI355X (256 MB): a call whose chunk records fit it streams
+// prep's inputs past it, so that the records stay there for the passes that read them.
+constexpr size_t kMallBytes = size_t(256) << 20;
 // Device address of that device's copy of the workspace, resolved once per device with the
 // device current (0 on success, else a HIP error code).
 int scratch_address(int device, void** ptr);

@@ -32,6 +32,8 @@
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -119,21 +121,28 @@ __device__ __forceinline__ void load_inputs(const Plan& p, const Item& it, int w
                                rv = rows_rsrc(p.v, it, H, it.h, 2), rg = rows_rsrc(p.g_raw, it, H, it.h, GF32 ? 4 : 2);
   const int row2 = H * kHead * 2;  // bytes per token row of a 2-byte [T][H][128] tensor
   // The whole offset goes in the vector operand: the range check covers only that part.
+  // The cache policy is an instruction immediate: one copy of the loads per policy, chosen
+  // by a uniform branch (both copies issue the same loads, so no wait is forced at the join).
+  auto issue = [&](auto policy) {
+    constexpr int kPolicy = decltype(policy)::value;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int vo = (8 * w + i) * row2 + lane * 4;
-    const int vqk = GVA ? (8 * w + i) * Hqk * kHead * 2 + lane * 4 : vo;
-    in.q[i] = __builtin_amdgcn_raw_buffer_load_b32(rq, vqk, 0, kStreamLoad);
-    in.k[i] = __builtin_amdgcn_raw_buffer_load_b32(rk, vqk, 0, kStreamLoad);
-    in.v[i] = __builtin_amdgcn_raw_buffer_load_b32(rv, vo, 0, kStreamLoad);
-    if constexpr (GF32) {
-      const auto g = __builtin_amdgcn_raw_buffer_load_b64(rg, 2 * vo, 0, kStreamLoad);
-      in.g[i] = make_float2(__uint_as_float(g[0]), __uint_as_float(g[1]));
-    } else {
-      const uint32_t g = __builtin_amdgcn_raw_buffer_load_b32(rg, vo, 0, kStreamLoad);
-      in.g[i] = make_float2(__uint_as_float(g << 16), __uint_as_float(g & 0xffff0000u));
+    for (int i = 0; i < 8; ++i) {
+      const int vo = (8 * w + i) * row2 + lane * 4;
+      const int vqk = GVA ? (8 * w + i) * Hqk * kHead * 2 + lane * 4 : vo;
+      in.q[i] = __builtin_amdgcn_raw_buffer_load_b32(rq, vqk, 0, kPolicy);
+      in.k[i] = __builtin_amdgcn_raw_buffer_load_b32(rk, vqk, 0, kPolicy);
+      in.v[i] = __builtin_amdgcn_raw_buffer_load_b32(rv, vo, 0, kPolicy);
+      if constexpr (GF32) {
+        const auto g = __builtin_amdgcn_raw_buffer_load_b64(rg, 2 * vo, 0, kPolicy);
+        in.g[i] = make_float2(__uint_as_float(g[0]), __uint_as_float(g[1]));
+      } else {
+        const uint32_t g = __builtin_amdgcn_raw_buffer_load_b32(rg, vo, 0, kPolicy);
+        in.g[i] = make_float2(__uint_as_float(g << 16), __uint_as_float(g & 0xffff0000u));
+      }
     }
-  }
+  };
+  if (p.stream_inputs) issue(std::integral_constant<int, kStreamLoad>{});
+  else issue(std::integral_constant<int, 0>{});
   // Raw beta of row 8w + (lane & 7) as two 2-byte loads (the upper and lower halves of
   // an fp32 value, or the bf16 value twice), so no branch holds the loads back and no
   // byte outside the element is read.
