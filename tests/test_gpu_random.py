@@ -6,10 +6,15 @@ state mode (none, dense, paged with padded strides and mixed has_initial_state f
 state dtype and plane order, gate and beta dtypes, and the gate's lower bound and shift.
 Every case is checked per (sequence, head) against the oracle, and paged cases also for
 untouched slots. The cases are fixed by their seeds, so a failure names a reproducible
-call."""
+call. A second set forces each value-channel split (KDA_DV_SPLIT: the narrow and
+whole-head scan kernels) and, for every third case, 8-chunk segments (KDA_SEG_LEN), so
+that the segment maps and their combine also see these shapes."""
+import os
+
 import numpy as np
 import pytest
 
+import gated_delta_rule_pack_amd as kda
 from gated_delta_rule_pack_amd.workloads import make_workload
 from tests.kda_harness import compare, run_gpu, untouched_slots_bitwise
 
@@ -62,6 +67,40 @@ def test_random_call_matches_oracle(case):
     print(f"case {case}: {kw}", flush=True)
     wl = make_workload(f"random_{case}", **kw)
     run = run_gpu(wl)
+    compare(wl, run)
+    if wl.state_mode == "paged":
+        untouched_slots_bitwise(wl, run)
+
+
+_CONTEXTS = {}
+
+
+def _context(**env):
+    """A context created with tuning overrides in the environment (restored after)."""
+    key = tuple(sorted(env.items()))
+    if key not in _CONTEXTS:
+        old = {k: os.environ.get(k) for k in env}
+        os.environ.update({k: str(v) for k, v in env.items()})
+        try:
+            _CONTEXTS[key] = kda.Context(0)
+        finally:
+            for k, v in old.items():
+                if v is None:
+                    del os.environ[k]
+                else:
+                    os.environ[k] = v
+    return _CONTEXTS[key]
+
+
+@pytest.mark.parametrize("case", range(16))
+def test_random_call_forced_kernels_matches_oracle(case):
+    kw = _draw(100 + case)
+    env = {"KDA_DV_SPLIT": (1, 2, 4, 8)[case % 4]}
+    if case % 3 == 0:
+        env["KDA_SEG_LEN"] = 8
+    print(f"case {100 + case} with {env}: {kw}", flush=True)
+    wl = make_workload(f"random_forced_{case}", **kw)
+    run = run_gpu(wl, context=_context(**env))
     compare(wl, run)
     if wl.state_mode == "paged":
         untouched_slots_bitwise(wl, run)
