@@ -194,33 +194,47 @@ __device__ __forceinline__ void st_col8(char* lds, int off, int c, int w, const 
   *reinterpret_cast<uint4*>(lds + off + (c * LDT + 8 * w) * 2) = uint4{v[0], v[1], v[2], v[3]};
 }
 
-// Sum 16 per-lane values over the 64 lanes of a wave with 17 exchanges: each step keeps
-// half of the values and adds the partner's copy of that half. Lane L ends up holding
-// the total of value index 8*b5 + 4*b4 + 2*b3 + b2 (b = bits of L).
+// Sum 16 per-lane values over the 64 lanes of a wave. Each step keeps half of the values
+// and adds the partner's copy of that half; every exchange is a lane permutation on the
+// vector ALU (no LDS round trip). Steps over lane bits 5 and 4 swap a pair of registers
+// between half-waves (v_permlane32_swap) and between 16-lane rows (v_permlane16_swap),
+// which moves both halves at once; bit 3 pairs lanes across each row (row rotate by 8);
+// bit 2 pairs lane i with 7 - i of its eight (half-row mirror), and the last two steps
+// sum each quad. Lane L ends up holding the total of value index 8*b5 + 4*b4 + 2*b3 + b2
+// (b = bits of L).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+constexpr int kDppRowRor8 = 0x128;
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppQuadXor2 = 0x4e;  // quad_perm [2, 3, 0, 1]
+constexpr int kDppQuadXor1 = 0xb1;  // quad_perm [1, 0, 3, 2]
+
 __device__ __forceinline__ float wave_sum16(const float* x, int lane) {
-  const bool b5 = lane & 32, b4 = lane & 16, b3 = lane & 8, b2 = lane & 4;
+  const bool b3 = lane & 8, b2 = lane & 4;
   float y[8], z[4], u[2];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const float keep = b5 ? x[8 + j] : x[j];
-    const float send = b5 ? x[j] : x[8 + j];
-    y[j] = keep + __shfl_xor(send, 32);
+    // Lanes 0..31 keep value j, lanes 32..63 value 8 + j.
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x[j]), __float_as_uint(x[8 + j]), false, false);
+    y[j] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
   }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const float keep = b4 ? y[4 + j] : y[j];
-    const float send = b4 ? y[j] : y[4 + j];
-    z[j] = keep + __shfl_xor(send, 16);
+    // Even rows keep y[j], odd rows y[4 + j].
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(y[j]), __float_as_uint(y[4 + j]), false, false);
+    z[j] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
   }
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const float keep = b3 ? z[2 + j] : z[j];
     const float send = b3 ? z[j] : z[2 + j];
-    u[j] = keep + __shfl_xor(send, 8);
+    u[j] = keep + dpp<kDppRowRor8>(send);
   }
-  float s = (b2 ? u[1] : u[0]) + __shfl_xor(b2 ? u[0] : u[1], 4);
-  s += __shfl_xor(s, 2);
-  s += __shfl_xor(s, 1);
+  float s = (b2 ? u[1] : u[0]) + dpp<kDppRowHalfMirror>(b2 ? u[0] : u[1]);
+  s += dpp<kDppQuadXor2>(s);
+  s += dpp<kDppQuadXor1>(s);
   return s;
 }
 
