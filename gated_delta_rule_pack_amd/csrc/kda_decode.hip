@@ -35,14 +35,35 @@ namespace {
 constexpr int kRowsPerWave = 32;
 constexpr int kIters = kRowsPerWave / 4;  // four rows per wave per iteration
 
-// Sum over the 16 lanes of a row group (lanes 16r .. 16r+15).
+// Sum over the 16 lanes of a row group (lanes 16r .. 16r+15), left in every lane of the
+// group. Each step adds a lane permutation of the partial sums on the vector ALU (DPP, no
+// LDS round trip): quad partners at distance 1 and 2, then lane i with 7 - i of its eight
+// (the two quads of a half-row), then the two half-rows (row rotate by 8).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, false));
+}
 __device__ __forceinline__ float sum16(float x) {
-  x += __shfl_xor(x, 1);
-  x += __shfl_xor(x, 2);
-  x += __shfl_xor(x, 4);
-  x += __shfl_xor(x, 8);
+  x += dpp<0xb1>(x);   // quad_perm [1, 0, 3, 2]
+  x += dpp<0x4e>(x);   // quad_perm [2, 3, 0, 1]
+  x += dpp<0x141>(x);  // row_half_mirror
+  x += dpp<0x128>(x);  // row_ror:8
   return x;
 }
+
+// x plus its copy in lane l ^ 8, l ^ 16 or l ^ 32 (row rotate by 8; the row and half-wave
+// register swaps of gfx950, which here swap a register with itself).
+__device__ __forceinline__ float add_xor8(float x) { return x + dpp<0x128>(x); }
+__device__ __forceinline__ float add_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float add_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// Sum over all 64 lanes, left in every lane.
+__device__ __forceinline__ float sum64(float x) { return add_xor32(add_xor16(sum16(x))); }
 
 __device__ __forceinline__ float sigmoid(float x) { return 1.0f / (1.0f + __expf(-x)); }
 
@@ -366,11 +387,8 @@ __global__ __launch_bounds__(256) void decode_kfirst2_kernel(Plan p) {
                bf16_bits_to_f32(qw >> 16) * bf16_bits_to_f32(qw >> 16);
     float sk = bf16_bits_to_f32(kw & 0xffffu) * bf16_bits_to_f32(kw & 0xffffu) +
                bf16_bits_to_f32(kw >> 16) * bf16_bits_to_f32(kw >> 16);
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) {
-      sq += __shfl_xor(sq, m);
-      sk += __shfl_xor(sk, m);
-    }
+    sq = sum64(sq);
+    sk = sum64(sk);
     const float rq = rsqrtf(sq + 1e-6f) * p.scale;  // scale folded into q-hat
     const float rk = rsqrtf(sk + 1e-6f);
     float qh[kIters], kh[kIters], eg[kIters];
@@ -399,11 +417,7 @@ __global__ __launch_bounds__(256) void decode_kfirst2_kernel(Plan p) {
       for (int j = 0; j < 8; ++j) pu[j] += row8_get<SDT>(raw[i], j) * w;
     }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      pu[j] += __shfl_xor(pu[j], 8);
-      pu[j] += __shfl_xor(pu[j], 16);
-      pu[j] += __shfl_xor(pu[j], 32);
-    }
+    for (int j = 0; j < 8; ++j) pu[j] = add_xor32(add_xor16(add_xor8(pu[j])));
     if (ko == 0)
 #pragma unroll
       for (int j = 0; j < 8; ++j) part[0][half][c0 + j] = pu[j];
@@ -427,11 +441,7 @@ __global__ __launch_bounds__(256) void decode_kfirst2_kernel(Plan p) {
       if (out_plane) store_row8<SDT>(out_plane, (size_t)(r0 + 8 * i) * kHead + c0, x);
     }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      po[j] += __shfl_xor(po[j], 8);
-      po[j] += __shfl_xor(po[j], 16);
-      po[j] += __shfl_xor(po[j], 32);
-    }
+    for (int j = 0; j < 8; ++j) po[j] = add_xor32(add_xor16(add_xor8(po[j])));
     if (ko == 0)
 #pragma unroll
       for (int j = 0; j < 8; ++j) part[1][half][c0 + j] = po[j];
