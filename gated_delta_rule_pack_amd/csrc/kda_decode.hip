@@ -21,7 +21,7 @@
 // sixteen lanes per row and eight keys per lane (one or two 16-byte accesses). Every
 // row's loads are issued before any of its arithmetic, the rows stay packed at the
 // storage dtype until they are used, and the two row reductions (u and o) are 16-lane
-// butterflies.
+// sums on DPP lane permutes.
 
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
