@@ -1,5 +1,6 @@
-"""Host-side pieces of bench.py: the per-launch byte and flop counts, and the refusal of
-more than one GPU. No GPU is touched."""
+"""Host-side pieces of bench.py: the per-launch byte and flop counts, the refusal of more
+than one GPU, and that the committed traffic summaries match the kernel sources. No GPU
+is touched."""
 import os
 import subprocess
 import sys
@@ -55,3 +56,18 @@ def test_grouped_heads_read_fewer_qk_bytes():
     th = 4096 * 12
     assert bench.kernel_bytes(f, "call", 128) - bench.kernel_bytes(g, "call", 128) == th * 256
     assert bench.kernel_bytes(f, "scan", 128) == bench.kernel_bytes(g, "scan", 128)
+
+
+def test_committed_traffic_profiles_match_the_kernel_sources():
+    """Every committed HBM-traffic summary was taken from the kernel sources as they are
+    now (the bench reports traffic only from a matching summary)."""
+    import glob
+    import os
+    import re
+    files = sorted(glob.glob(os.path.join(bench.ROOT, "profiles", "kda_*_traffic_*.txt")))
+    assert files
+    for path in files:
+        kernel = os.path.basename(path)[len("kda_"):].split("_traffic_")[0]
+        m = re.search(r"source_sha256_16:\s*([0-9a-f]+)", open(path).read())
+        assert m, path
+        assert m.group(1) == bench.kernel_source_hash(kernel), f"{path} was taken from other {kernel} sources"
