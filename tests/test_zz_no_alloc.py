@@ -4,8 +4,11 @@ Two calls in a row through the fixed per-device workspace, the second smaller th
 first (the workspace keeps the first call's bytes), then a segmented call, a decode call
 and a dense call with a final state: each equals kda_chunk_fwd on the same inputs bit
 for bit (the same kernels run on the same bytes), and is on the oracle. Nothing is
-allocated: torch's allocated bytes do not move and the library's arenas do not grow. A
-call that does not fit the workspace is refused before anything is enqueued.
+allocated: torch's count of device allocations does not move and the library's arenas
+do not grow. A call that does not fit the workspace is refused before anything is
+enqueued. Eight seeded
+mixed calls (every state mode and dtype, plane order, grouped heads) equal kda_chunk_fwd
+bit for bit as well.
 """
 import numpy as np
 import pytest
@@ -23,6 +26,15 @@ def _say(msg):
     print(msg, flush=True)
 
 
+def _alloc_count():
+    """Device allocation requests torch's allocator has served so far."""
+    st = torch.cuda.memory_stats()
+    for key in ("allocation.all.allocated", "allocated.all.allocated"):
+        if key in st:
+            return st[key]
+    raise KeyError("torch.cuda.memory_stats() reports no allocation count")
+
+
 def _noalloc(wl, ctx):
     d = device_inputs(wl)
     out = torch.full_like(d["v"], float("nan"))
@@ -30,15 +42,19 @@ def _noalloc(wl, ctx):
     kw = dict(cu_seqlens_cpu=wl.cu_seqlens, scale=wl.scale, lower_bound=wl.lower_bound,
               state_k_first=wl.state_k_first, context=ctx)
     if wl.state_mode == "dense":
-        fin = torch.full_like(d["initial_state"], float("nan"))
-        kw.update(initial_state=d["initial_state"], final_state=fin)
+        kw.update(initial_state=d["initial_state"])
+        if wl.want_final_state:
+            fin = torch.full_like(d["initial_state"], float("nan"))
+            kw.update(final_state=fin)
     elif wl.state_mode == "paged":
         kw.update(state_cache=d["state_cache"], state_indices=d["state_indices"],
                   has_initial_state=d["has_initial_state"])
     torch.cuda.synchronize()
-    before = torch.cuda.memory_allocated()
+    # The cumulative count of torch's device allocations: unlike the bytes in use, a free of
+    # some unrelated tensor (a garbage collection during the call) cannot hide an allocation.
+    before = _alloc_count()
     kda.chunk_fwd_noalloc(d["q"], d["k"], d["v"], d["g_raw"], d["beta_raw"], d["cu_seqlens"], out=out, **kw)
-    assert torch.cuda.memory_allocated() == before, "the allocation-free call allocated through torch"
+    assert _alloc_count() == before, "the allocation-free call allocated through torch"
     torch.cuda.synchronize()
     return GpuRun(to_f64(out[0]), to_f64(fin) if fin is not None else None,
                   d["storage"].cpu() if wl.state_mode == "paged" else None)
@@ -98,4 +114,21 @@ def test_noalloc_refuses_a_call_beyond_the_workspace():
     torch.cuda.synchronize()
     assert torch.isnan(out).all() and torch.equal(d["storage"].view(torch.int32), pool_before.view(torch.int32))
     assert ctx.stats()["calls"] == 0
+    ctx.close()
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_noalloc_random_calls_equal_chunk_fwd(case):
+    """Seeded mixed calls (the generator of test_gpu_random): the allocation-free entry
+    point equals kda_chunk_fwd bit for bit and allocates nothing."""
+    from tests.test_gpu_random import _draw
+    kw = _draw(200 + case)
+    _say(f"case {200 + case}: {kw}")
+    wl = make_workload(f"noalloc_random_{case}", **kw)
+    ctx = kda.Context(0)
+    ref = run_gpu(wl, context=kda.get_context("cuda"))
+    grows = ctx.stats()["arena_grows"]
+    got = _noalloc(wl, ctx)
+    _same(wl, got, ref)
+    assert ctx.stats()["arena_grows"] == grows
     ctx.close()
