@@ -69,6 +69,53 @@ struct Unit {
                        // (-1: last segment); map: the map slot
 };
 
+// The chunk's decay exp(G_C) for the state rows a lane holds. A lane's rows are keys
+// k = 16*tt + 4*g4 + i (key tile tt, register i), so the 16 lanes of a row g4 all need
+// the same 32 keys and the wave only 128. Each lane reads two of its row's keys,
+// 16*(j/4) + 4*g4 + j%4 and the same + 64 (j = lane within the row), and the decay of
+// key tile tt, register i is broadcast along the row from lane 4*(tt%4) + i, register
+// tt/4 (DPP row_newbcast, folded into the multiply): one two-word LDS read per step in
+// place of eight 16-byte ones, and no more VALU instructions.
+__device__ __forceinline__ void read_decay(float (&e)[2], const char* slot_e, int g4, int l16) {
+  const float* E = reinterpret_cast<const float*>(slot_e) + 16 * (l16 >> 2) + 4 * g4 + (l16 & 3);
+  e[0] = E[0];
+  e[1] = E[64];
+}
+
+template <int J>
+__device__ __forceinline__ float row_bcast(float x) {
+  // Every lane's source (lane J of its row) exists, so bound_ctrl does not matter; set,
+  // it lets the compiler fold the move into the multiply.
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x150 + J, 0xf, 0xf, true));
+}
+
+// S^T[k][v] *= exp(G_C)[k] for key tiles TT..7.
+template <int TT = 0>
+__device__ __forceinline__ void decay_state(f32x4 (&S)[8], const float (&e)[2]) {
+  if constexpr (TT < 8) {
+    constexpr int J = 4 * (TT & 3);
+    S[TT][0] *= row_bcast<J + 0>(e[TT >> 2]);
+    S[TT][1] *= row_bcast<J + 1>(e[TT >> 2]);
+    S[TT][2] *= row_bcast<J + 2>(e[TT >> 2]);
+    S[TT][3] *= row_bcast<J + 3>(e[TT >> 2]);
+    decay_state<TT + 1>(S, e);
+  }
+}
+
+// A operand that copies U into the Delta accumulators on the matrix unit instead of
+// widening it on the vector ALU. The U fragment, taken as a B operand, holds in element
+// j of lane group g the chunk row 16*(j/4) + 4g + j%4 (the accumulator rows of both row
+// tiles). Row m of u_select(t) has a single 1, at the element that holds row 16t + m, so
+// mfma(u_select(t), U, 0) is rows 16t..16t+15 of U, exactly and in accumulator layout;
+// the W products then accumulate onto the same fp32 values as before.
+__device__ __forceinline__ bf16x8 u_select(int t, int g4, int l16) {
+  const int d = l16 - 4 * g4;  // row l16 sits in element d + 4t of group g4 if 0 <= d < 4
+  bf16x8 a;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) a[j] = to_bf16(d >= 0 && d < 4 && j == d + 4 * t ? 1.f : 0.f);
+  return a;
+}
+
 // Workgroups are dealt round-robin to the 8 XCDs; all groups of one unit land on one
 // XCD, so its records are fetched into that XCD's L2 once. Scan: units are (segment,
 // head), groups the value-channel halves. Map: units are (map slot, head), groups the
@@ -216,12 +263,13 @@ __global__ __launch_bounds__(320, 1) void head_kernel(Plan p, int units, int gro
   // Ring reads, issued together in order of first use and pinned in that order (the
   // scheduler would otherwise sink each read to its use or permute them): the LDS
   // counter can name at most 15 reads in flight, so the wait before the first MFMA then
-  // covers W, U and little else.
+  // covers W, U and little else. (Reading U first, as the narrow kernel does, measured
+  // slower in this kernel.)
   struct Frags {
     bf16x8 w[2][4];  // -W (row tile t, key block m)
     bf16x8 u[NTW];   // U of this wave's value tiles
     bf16x8 k[8];     // K (key tile)
-    f32x4 e[8];      // exp(G_C) of this lane's keys 16*tt + 4*g4 + i
+    float e[2];      // exp(G_C), two keys of this lane's row (read_decay)
   };
   auto read = [&](Frags& f, const char* sl) {
     __builtin_amdgcn_sched_barrier(0);
@@ -244,14 +292,12 @@ __global__ __launch_bounds__(320, 1) void head_kernel(Plan p, int units, int gro
       f.k[tt] = *reinterpret_cast<const bf16x8*>(sl + L::kSlotK + tt * 1024 + vo);
       __builtin_amdgcn_sched_barrier(0);
     }
-#pragma unroll
-    for (int tt = 0; tt < 8; ++tt) {
-      f.e[tt] = *reinterpret_cast<const f32x4*>(sl + L::kSlotE + (16 * tt + 4 * g4) * 4);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    read_decay(f.e, sl + L::kSlotE, g4, l16);
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   const size_t row_stride = (size_t)p.H * kHead;
+  const bf16x8 usel[2] = {u_select(0, g4, l16), u_select(1, g4, l16)};
   if (nc > 0) {
     barrier_lds();  // the loader has chunk 0 in slot 0
     Frags f;
@@ -265,24 +311,21 @@ __global__ __launch_bounds__(320, 1) void head_kernel(Plan p, int units, int gro
       for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
         for (int m = 0; m < 4; ++m) Sb[nt][m] = pack8(S[nt][2 * m], S[nt][2 * m + 1]);
-      // Delta = U + (-W) S^T, accumulated from U; rows {4g..4g+3, 16+4g..16+4g+3}.
+      // Delta = U + (-W) S^T, accumulated from U (copied in by an MFMA); rows
+      // {4g..4g+3, 16+4g..16+4g+3}.
       f32x4 x[NTW][2];
 #pragma unroll
       for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-          f32x4 a;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) a[i] = from_bf16(f.u[nt][4 * t + i]);
+          f32x4 a = mfma(usel[t], f.u[nt], zero4());
 #pragma unroll
           for (int m = 0; m < 4; ++m) a = mfma(f.w[t][m], Sb[nt][m], a);
           x[nt][t] = a;
         }
       // Diag(E) S^T while the MFMAs above run.
 #pragma unroll
-      for (int nt = 0; nt < NTW; ++nt)
-#pragma unroll
-        for (int tt = 0; tt < 8; ++tt) S[nt][tt] = S[nt][tt] * f.e[tt];
+      for (int nt = 0; nt < NTW; ++nt) decay_state(S[nt], f.e);
       bf16x8 Db[NTW];
 #pragma unroll
       for (int nt = 0; nt < NTW; ++nt) Db[nt] = pack8(x[nt][0], x[nt][1]);
@@ -522,42 +565,40 @@ __global__ __launch_bounds__(256, 1) void scan_narrow(Plan p, int units, int gro
 
     // One chunk's fragments, read from its ring slot.
     // Issued together, in order of first use and pinned in that order (the scheduler
-    // would otherwise sink each read to its use or permute them): the LDS counter can
-    // name at most 15 reads in flight, so the wait before the first MFMA then covers
-    // only W, U and little else.
+    // would otherwise sink each read to its use or permute them): U, which the first
+    // MFMA of each Delta chain copies, then W by key block, both row tiles' fragments of
+    // a block together, so that both chains start while the rest of W, K and E land.
     struct Frags {
       bf16x8 w[2][4];  // -W (row tile t, key block m)
       bf16x8 u[NT];    // U of this workgroup's value tiles
       bf16x8 k[8];     // K (key tile)
-      f32x4 e[8];      // exp(G_C) of this lane's keys 16*tt + 4*g4 + i
+      float e[2];      // exp(G_C), two keys of this lane's row (read_decay)
     };
     auto read = [&](Frags& f, int slot) {
       const char* sl = lds + slot * L::kSlot;
       __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          f.w[t][m] = *reinterpret_cast<const bf16x8*>(sl + L::kSlotW + (t * 4 + m) * 1024 + vo);
-          __builtin_amdgcn_sched_barrier(0);
-        }
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         f.u[nt] = *reinterpret_cast<const bf16x8*>(sl + L::kSlotU + nt * 1024 + vo);
         __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          f.w[t][m] = *reinterpret_cast<const bf16x8*>(sl + L::kSlotW + (t * 4 + m) * 1024 + vo);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
       for (int tt = 0; tt < 8; ++tt) {
         f.k[tt] = *reinterpret_cast<const bf16x8*>(sl + L::kSlotK + tt * 1024 + vo);
         __builtin_amdgcn_sched_barrier(0);
       }
-#pragma unroll
-      for (int tt = 0; tt < 8; ++tt) {
-        f.e[tt] = *reinterpret_cast<const f32x4*>(sl + L::kSlotE + (16 * tt + 4 * g4) * 4);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+      read_decay(f.e, sl + L::kSlotE, g4, l16);
+      __builtin_amdgcn_sched_barrier(0);
     };
 
+    const bf16x8 usel[2] = {u_select(0, g4, l16), u_select(1, g4, l16)};
     if (nc > 0) {
       barrier_lds();  // the loader has chunk 0 in slot 0
       Frags f;
@@ -572,16 +613,14 @@ __global__ __launch_bounds__(256, 1) void scan_narrow(Plan p, int units, int gro
         for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
           for (int m = 0; m < 4; ++m) Sb[nt][m] = pack8(S[nt][2 * m], S[nt][2 * m + 1]);
-        // Delta = U + (-W) S^T, accumulated from U; rows {4g..4g+3, 16+4g..16+4g+3} of
-        // the chunk per lane.
+        // Delta = U + (-W) S^T, accumulated from U (copied in by an MFMA); rows
+        // {4g..4g+3, 16+4g..16+4g+3} of the chunk per lane.
         f32x4 x[NT][2];
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
           for (int t = 0; t < 2; ++t) {
-            f32x4 a;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) a[i] = from_bf16(f.u[nt][4 * t + i]);
+            f32x4 a = mfma(usel[t], f.u[nt], zero4());
 #pragma unroll
             for (int m = 0; m < 4; ++m) a = mfma(f.w[t][m], Sb[nt][m], a);
             x[nt][t] = a;
@@ -593,9 +632,7 @@ __global__ __launch_bounds__(256, 1) void scan_narrow(Plan p, int units, int gro
           for (int m = 0; m < 4; ++m) *reinterpret_cast<bf16x8*>(lds + L::sb(par, nt, m) + vo) = Sb[nt][m];
         // Diag(E) S^T while the MFMAs above run.
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-          for (int tt = 0; tt < 8; ++tt) S[nt][tt] = S[nt][tt] * f.e[tt];
+        for (int nt = 0; nt < NT; ++nt) decay_state(S[nt], f.e);
         bf16x8 Db[NT];
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
