@@ -24,10 +24,11 @@
 // The products run on bf16 MFMA with hi/lo operand splits and fp32 accumulation.
 //
 // Organisation: a persistent grid (two workgroups per CU) walks the items; each
-// workgroup loads the next item's inputs while it computes the current one. Thread
-// (wave w, lane l) owns rows 8w .. 8w+7 and key/value channels 2l, 2l+1, so the in-chunk
-// cumsum is mostly in registers and transposed tiles are written 16 bytes at a time.
-// Output: one record per (head, chunk) in the scan's MFMA fragment order.
+// workgroup loads the next item's inputs while it computes the current one. Eight waves
+// share an item, so each SIMD holds four waves to cover the latency of the item's phases.
+// Thread (wave w, lane l) owns rows 4w .. 4w+3 and key/value channels 2l, 2l+1, so the
+// in-chunk cumsum is mostly in registers and transposed tiles are written 8 bytes at a
+// time. Output: one record per (head, chunk) in the scan's MFMA fragment order.
 
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
@@ -44,10 +45,15 @@ constexpr int LDA = 136;   // bf16 per row of a [32][128] operand tile (16-byte 
 constexpr int LDT = 40;    // bf16 per row of a transposed [128][32] tile
 constexpr int LDF = 36;    // fp32 per row of the [32][32] A / P / T tiles
 
+constexpr int kWaves = kThreadsPrep / 64;  // waves per item
+constexpr int kRows = kChunk / kWaves;      // rows per wave
+static_assert(kRows == 4, "the thread layout below is written for four rows per wave");
+
 // Region A: small per-item tiles.
-constexpr int kOffTot = 0;                      // fp32 [4][128] per-wave cumsum totals
-constexpr int kOffBeta = kOffTot + 4 * 128 * 4; // fp32 [32]
+constexpr int kOffBeta = 0;                     // fp32 [32]
 constexpr int kOffA = kOffBeta + 32 * 4;        // fp32 [32][LDF]
+constexpr int kOffTot = kOffA;                  // fp32 [8][128] per-wave cumsum totals,
+                                                // dead before A is written
 constexpr int kOffP = kOffA + 32 * LDF * 4;     // fp32 [32][LDF]
 constexpr int kOffT = kOffP + 32 * LDF * 4;     // fp32 [32][LDF] T = (I + A)^{-1}
 constexpr int kOffM = kOffT + 32 * LDF * 4;     // fp32 [16][LDF] scratch of the block solve
@@ -68,6 +74,7 @@ constexpr int lds_bytes(int ref) {
   return off_x(ref) + (factor_bytes(ref) > kProductBytes ? factor_bytes(ref) : kProductBytes);
 }
 static_assert(2 * lds_bytes(16) <= 160 * 1024, "two workgroups per CU at the default block");
+static_assert(kWaves * 128 * 4 <= 32 * LDF * 4, "the cumsum totals fit the A tile");
 
 // Offsets inside region X.
 constexpr int xLKh = 0, xLKl = xLKh + kTileA, xLQh = xLKl + kTileA, xLQl = xLQh + kTileA, xRh = xLQl + kTileA,
@@ -77,11 +84,11 @@ constexpr int xR0h = xRl + kTileA, xR0l = xR0h + kTileA / 2;
 constexpr int xKGh = 0, xKGl = xKGh + kTileT, xKt = xKGl + kTileT, xVt = xKt + kTileT, xQs = xVt + kTileT,
               xTh = xQs + kTileA, xTl = xTh + kTileTT;
 
-// Inputs of one item held by one thread: rows 8w .. 8w+7, channels 2l, 2l+1.
+// Inputs of one item held by one thread: rows 4w .. 4w+3, channels 2l, 2l+1.
 struct Inputs {
-  uint32_t q[8], k[8], v[8];  // two bf16 each
-  float2 g[8];                // raw gate (fp32, or bf16 widened on load)
-  float braw;                 // raw beta of row 8w + (lane & 7) (lanes 0..7 meaningful)
+  uint32_t q[4], k[4], v[4];  // two bf16 each
+  float2 g[4];                // raw gate (fp32, or bf16 widened on load)
+  float braw;                 // raw beta of row 4w + (lane & 3) (lanes 0..3 meaningful)
 };
 
 struct Item {
@@ -126,9 +133,9 @@ __device__ __forceinline__ void load_inputs(const Plan& p, const Item& it, int w
   auto issue = [&](auto policy) {
     constexpr int kPolicy = decltype(policy)::value;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int vo = (8 * w + i) * row2 + lane * 4;
-      const int vqk = GVA ? (8 * w + i) * Hqk * kHead * 2 + lane * 4 : vo;
+    for (int i = 0; i < 4; ++i) {
+      const int vo = (4 * w + i) * row2 + lane * 4;
+      const int vqk = GVA ? (4 * w + i) * Hqk * kHead * 2 + lane * 4 : vo;
       in.q[i] = __builtin_amdgcn_raw_buffer_load_b32(rq, vqk, 0, kPolicy);
       in.k[i] = __builtin_amdgcn_raw_buffer_load_b32(rk, vqk, 0, kPolicy);
       in.v[i] = __builtin_amdgcn_raw_buffer_load_b32(rv, vo, 0, kPolicy);
@@ -143,10 +150,10 @@ __device__ __forceinline__ void load_inputs(const Plan& p, const Item& it, int w
   };
   if (p.stream_inputs) issue(std::integral_constant<int, kStreamLoad>{});
   else issue(std::integral_constant<int, 0>{});
-  // Raw beta of row 8w + (lane & 7) as two 2-byte loads (the upper and lower halves of
+  // Raw beta of row 4w + (lane & 3) as two 2-byte loads (the upper and lower halves of
   // an fp32 value, or the bf16 value twice), so no branch holds the loads back and no
   // byte outside the element is read.
-  const int brow = min(it.t0 + 8 * w + (lane & 7), p.T - 1);
+  const int brow = min(it.t0 + 4 * w + (lane & 3), p.T - 1);
   const size_t bidx = (size_t)brow * H + it.h;
   const bool bf = p.beta_dtype != kF32;
   const char* bb = reinterpret_cast<const char*>(p.beta_raw);
@@ -188,20 +195,26 @@ __device__ __forceinline__ bf16x8 ld_frag_2x4(const char* lds, int off0, int off
   return __builtin_bit_cast(bf16x8, r);
 }
 
-// Write 8 bf16 (one channel, rows 8w .. 8w+7, packed two rows a word) to a transposed
-// [128][LDT] tile.
-__device__ __forceinline__ void st_col8(char* lds, int off, int c, int w, const uint32_t* v) {
-  *reinterpret_cast<uint4*>(lds + off + (c * LDT + 8 * w) * 2) = uint4{v[0], v[1], v[2], v[3]};
+// Write channels 2l and 2l + 1 (rows 4w .. 4w+3 each, packed two rows a word) to a
+// transposed [128][LDT] tile. Lanes with bit 3 set write the odd channel first, so that
+// the 16 lanes an 8-byte store serves at once spread over twice as many LDS banks.
+__device__ __forceinline__ void st_cols(char* lds, int off, int lane, int w, const uint32_t* a, const uint32_t* b) {
+  const int sw = (lane >> 3) & 1;
+  const int c = 2 * lane;
+  const uint2 x = sw ? uint2{b[0], b[1]} : uint2{a[0], a[1]};
+  const uint2 y = sw ? uint2{a[0], a[1]} : uint2{b[0], b[1]};
+  *reinterpret_cast<uint2*>(lds + off + ((c + sw) * LDT + 4 * w) * 2) = x;
+  *reinterpret_cast<uint2*>(lds + off + ((c + 1 - sw) * LDT + 4 * w) * 2) = y;
 }
 
-// Sum 16 per-lane values over the 64 lanes of a wave. Each step keeps half of the values
-// and adds the partner's copy of that half; every exchange is a lane permutation on the
-// vector ALU (no LDS round trip). Steps over lane bits 5 and 4 swap a pair of registers
-// between half-waves (v_permlane32_swap) and between 16-lane rows (v_permlane16_swap),
-// which moves both halves at once; bit 3 pairs lanes across each row (row rotate by 8);
-// bit 2 pairs lane i with 7 - i of its eight (half-row mirror), and the last two steps
-// sum each quad. Lane L ends up holding the total of value index 8*b5 + 4*b4 + 2*b3 + b2
-// (b = bits of L).
+// Sum 8 per-lane values over the 64 lanes of a wave. Each of the first three steps keeps
+// half of the values and adds the partner's copy of that half; every exchange is a lane
+// permutation on the vector ALU (no LDS round trip). Steps over lane bits 5 and 4 swap a
+// pair of registers between half-waves (v_permlane32_swap) and between 16-lane rows
+// (v_permlane16_swap), which moves both halves at once; bit 3 pairs lanes across each row
+// (row rotate by 8). The last three steps sum each group of eight lanes: lane i with
+// 7 - i (half-row mirror), then the quad permutes. Lane L ends up holding the total of
+// value index 4*b5 + 2*b4 + b3 (b = bits of L).
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, false));
@@ -211,28 +224,25 @@ constexpr int kDppRowHalfMirror = 0x141;
 constexpr int kDppQuadXor2 = 0x4e;  // quad_perm [2, 3, 0, 1]
 constexpr int kDppQuadXor1 = 0xb1;  // quad_perm [1, 0, 3, 2]
 
-__device__ __forceinline__ float wave_sum16(const float* x, int lane) {
-  const bool b3 = lane & 8, b2 = lane & 4;
-  float y[8], z[4], u[2];
+__device__ __forceinline__ float wave_sum8(const float* x, int lane) {
+  const bool b3 = lane & 8;
+  float y[4], z[2];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    // Lanes 0..31 keep value j, lanes 32..63 value 8 + j.
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x[j]), __float_as_uint(x[8 + j]), false, false);
+  for (int j = 0; j < 4; ++j) {
+    // Lanes 0..31 keep value j, lanes 32..63 value 4 + j.
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x[j]), __float_as_uint(x[4 + j]), false, false);
     y[j] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
   }
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    // Even rows keep y[j], odd rows y[4 + j].
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(y[j]), __float_as_uint(y[4 + j]), false, false);
+  for (int j = 0; j < 2; ++j) {
+    // Even rows keep y[j], odd rows y[2 + j].
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(y[j]), __float_as_uint(y[2 + j]), false, false);
     z[j] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
   }
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const float keep = b3 ? z[2 + j] : z[j];
-    const float send = b3 ? z[j] : z[2 + j];
-    u[j] = keep + dpp<kDppRowRor8>(send);
-  }
-  float s = (b2 ? u[1] : u[0]) + dpp<kDppRowHalfMirror>(b2 ? u[0] : u[1]);
+  const float keep = b3 ? z[1] : z[0];
+  const float send = b3 ? z[0] : z[1];
+  float s = keep + dpp<kDppRowRor8>(send);
+  s += dpp<kDppRowHalfMirror>(s);
   s += dpp<kDppQuadXor2>(s);
   s += dpp<kDppQuadXor1>(s);
   return s;
@@ -242,12 +252,13 @@ __device__ __forceinline__ float bcast(float x, int src) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), src));
 }
 
-__device__ __forceinline__ int lane_of_sum(int v) {
-  return ((v >> 3) & 1) * 32 + ((v >> 2) & 1) * 16 + ((v >> 1) & 1) * 8 + (v & 1) * 4;
-}
+__device__ __forceinline__ int lane_of_sum(int v) { return ((v >> 2) & 1) * 32 + ((v >> 1) & 1) * 16 + (v & 1) * 8; }
 
-template <int REF>
-__device__ void process_item(const Plan& p, const Item& it, const Inputs& in, char* lds, int w_in, int lane) {
+// Processes item it from its inputs in, and once they are dead (after staging) loads
+// the inputs of item next into in.
+template <int REF, bool GF32, bool GVA>
+__device__ void process_item(const Plan& p, const Item& it, Inputs& in, const Item& next, char* lds, int w_in,
+                             int lane) {
   // The wave index is uniform, so everything derived from it (fragment and tile choices,
   // LDS offsets, branch masks) is scalar. Redefining it here for the compiler keeps those
   // values from being hoisted out of the item loop, where they would stay live across
@@ -270,25 +281,25 @@ __device__ void process_item(const Plan& p, const Item& it, const Inputs& in, ch
   char* rec = reinterpret_cast<char*>(p.ws) + ((size_t)it.h * p.n_chunks + it.cid) * kRecBytes;
 
   // ---------------------------------------------------------------- elementwise
-  float qn[8][2], kn[8][2], G[8][2];
+  float qn[4][2], kn[4][2], G[4][2];
   {
-    float sq[16];
+    float sq[8];
     // Rows past the sequence were loaded as zeros.
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 4; ++i) {
       qn[i][0] = lo16(in.q[i]);
       qn[i][1] = hi16(in.q[i]);
       kn[i][0] = lo16(in.k[i]);
       kn[i][1] = hi16(in.k[i]);
       sq[i] = qn[i][0] * qn[i][0] + qn[i][1] * qn[i][1];
-      sq[8 + i] = kn[i][0] * kn[i][0] + kn[i][1] * kn[i][1];
+      sq[4 + i] = kn[i][0] * kn[i][0] + kn[i][1] * kn[i][1];
     }
     // Each lane takes the inverse norm of the row sum it holds; rows read theirs back.
-    const float rs = __builtin_amdgcn_rsqf(wave_sum16(sq, lane) + 1e-6f);
+    const float rs = __builtin_amdgcn_rsqf(wave_sum8(sq, lane) + 1e-6f);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 4; ++i) {
       const float rq = bcast(rs, lane_of_sum(i));
-      const float rk = bcast(rs, lane_of_sum(8 + i));
+      const float rk = bcast(rs, lane_of_sum(4 + i));
       qn[i][0] *= rq; qn[i][1] *= rq;
       kn[i][0] *= rk; kn[i][1] *= rk;
     }
@@ -297,15 +308,15 @@ __device__ void process_item(const Plan& p, const Item& it, const Inputs& in, ch
     const float lb2 = p.lower_bound * kLog2e;
     float run0 = 0.f, run1 = 0.f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const bool valid = 8 * w + i < len;
+    for (int i = 0; i < 4; ++i) {
+      const bool valid = 4 * w + i < len;
       run0 += valid ? lb2 * sigm(in.g[i].x) : 0.f;
       run1 += valid ? lb2 * sigm(in.g[i].y) : 0.f;
       G[i][0] = run0;
       G[i][1] = run1;
     }
     *reinterpret_cast<float2*>(tot + w * 128 + c0) = make_float2(run0, run1);
-    if (lane < 8) betas[8 * w + lane] = (8 * w + lane < len) ? sigm(in.braw) : 0.f;
+    if (lane < 4) betas[4 * w + lane] = (4 * w + lane < len) ? sigm(in.braw) : 0.f;
   }
   __syncthreads();
   {
@@ -317,13 +328,13 @@ __device__ void process_item(const Plan& p, const Item& it, const Inputs& in, ch
       o1 += t.y;
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 4; ++i) {
       G[i][0] += o0;
       G[i][1] += o1;
-      const int r = 8 * w + i;
+      const int r = 4 * w + i;
       if (r % REF == 0) *reinterpret_cast<float2*>(Gref + (r / REF) * 128 + c0) = make_float2(G[i][0], G[i][1]);
     }
-    if (w == 3) *reinterpret_cast<float2*>(Gref + NB * 128 + c0) = make_float2(G[7][0], G[7][1]);  // G_C
+    if (w == kWaves - 1) *reinterpret_cast<float2*>(Gref + NB * 128 + c0) = make_float2(G[3][0], G[3][1]);  // G_C
   }
   __syncthreads();
 
@@ -331,22 +342,22 @@ __device__ void process_item(const Plan& p, const Item& it, const Inputs& in, ch
   // At REF = 16 the record's Q, K and KG tiles are formed here from the decay factors
   // (e^{G_r} = e^{G_r - G_m} e^{G_m}, e^{G_C - G_r} = e^{G_C - G_16} e^{G_16 - G_r}, every
   // factor inside the fp32 range) and kept packed until staging.
-  [[maybe_unused]] uint32_t qs[8], kg0h[4], kg0l[4], kg1h[4], kg1l[4], kt0[4], kt1[4];
+  [[maybe_unused]] uint32_t qs[4], kg0h[2], kg0l[2], kg1h[2], kg1l[2], kt0[2], kt1[2];
   {
-    [[maybe_unused]] float kgv[8][2];
-    // The wave's 8 rows share one reference row when REF >= 8.
-    const float2 gw = *reinterpret_cast<const float2*>(Gref + (REF >= 8 ? (8 * w / REF) : 0) * 128 + c0);
+    [[maybe_unused]] float kgv[4][2];
+    // At REF = 16 the wave's 4 rows share one reference row (0 or 16).
+    const float2 gw = *reinterpret_cast<const float2*>(Gref + (REF == 16 ? w / 4 : 0) * 128 + c0);
     [[maybe_unused]] float em0 = 0.f, em1 = 0.f;
     if constexpr (REF == 16) {
       em0 = ex2(gw.x);  // e^{G_m}, m = 0 or 16: inside the fp32 range at REF = 16
       em1 = ex2(gw.y);
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = 8 * w + i;
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * w + i;
       // Below REF = 16 the rows of the lower half first take row 16 as their reference
       // (the pivot of the off-diagonal tile, see below).
-      const int gi = REF == 16 ? 0 : (w >= 2 ? 16 / REF : r / REF);
+      const int gi = REF == 16 ? 0 : (w >= kWaves / 2 ? 16 / REF : r / REF);
       const float2 gm = REF == 16 ? gw : *reinterpret_cast<const float2*>(Gref + gi * 128 + c0);
       const float e0 = ex2(G[i][0] - gm.x), e1 = ex2(G[i][1] - gm.y);  // in [e^-80, 1]
       uint32_t kh, kl, qh, ql;
@@ -366,19 +377,21 @@ __device__ void process_item(const Plan& p, const Item& it, const Inputs& in, ch
     }
     if constexpr (REF == 16) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < 2; ++j) {
         split2(kgv[2 * j][0], kgv[2 * j + 1][0], kg0h[j], kg0l[j]);
         split2(kgv[2 * j][1], kgv[2 * j + 1][1], kg1h[j], kg1l[j]);
       }
     }
   }
   const int l16 = lane & 15, g4 = lane >> 4;
-  // Tile jobs per wave: (row tile, column tile, matrix A=0 / P=1).
-  //   wave 0: (0,0,A) (0,0,P); wave 1: (1,0,A) (1,0,P); wave 2: (1,1,A); wave 3: (1,1,P)
-  const int njobs = (w < 2) ? 2 : 1;
-  const int jt = (w < 2) ? w : 1;
-  const int ja = (w < 2) ? 0 : 1;
-  f32x4 acc[2] = {zero4(), zero4()};
+  // One tile job for each of waves 0..5: (row tile jr, column tile jc, matrix A = 0 or
+  // P = 1): wave 0 (0,0,A), 1 (0,0,P), 2 (1,1,A), 3 (1,1,P), 4 (1,0,A), 5 (1,0,P). Waves 6
+  // and 7 write the zero tile (0,1) of A and of P.
+  const bool has_job = w < 6;
+  const int jr = w >= 2 ? 1 : 0;
+  const int jc = (w == 2 || w == 3) ? 1 : 0;
+  const int mat = w & 1;
+  f32x4 acc = zero4();
   if constexpr (REF == 16) {
     // Both row blocks at once. Row tile t is exactly row block t (reference row 16t),
     // so every job's rows are inside its block and no row masking is needed. Right
@@ -391,16 +404,17 @@ __device__ void process_item(const Plan& p, const Item& it, const Inputs& in, ch
       const float2 gc = *reinterpret_cast<const float2*>(Gref + NB * 128 + c0);
       const float d0 = ex2(g16.x - g0.x), d1 = ex2(g16.y - g0.y);  // e^{G_16 - G_0} <= 1
       const float c0e = ex2(gc.x - g16.x), c1e = ex2(gc.y - g16.y);  // e^{G_C - G_16} >= e^-80
-      float ktv[8][2];
+      const bool upper = w < kWaves / 2;  // rows 0..15
+      float ktv[4][2];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int r = 8 * w + i;
-        const float2 gm = (r < 16) ? g0 : g16;
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * w + i;
+        const float2 gm = upper ? g0 : g16;
         const float r0 = ex2(gm.x - G[i][0]), r1 = ex2(gm.y - G[i][1]);  // own block, <= e^80
         uint32_t h, l;
         const int o = (r * LDA + c0) * 2;
         float b0 = r0, b1 = r1;  // e^{G_16 - G_r}
-        if (r < 16) {
+        if (upper) {
           split2(kn[i][0] * r0, kn[i][1] * r1, h, l);
           *reinterpret_cast<uint32_t*>(X + xR0h + o) = h;
           *reinterpret_cast<uint32_t*>(X + xR0l + o) = l;
@@ -414,31 +428,26 @@ __device__ void process_item(const Plan& p, const Item& it, const Inputs& in, ch
         ktv[i][1] = kn[i][1] * (b1 * c1e);
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < 2; ++j) {
         kt0[j] = cvt_pk(ktv[2 * j][0], ktv[2 * j + 1][0]);
         kt1[j] = cvt_pk(ktv[2 * j][1], ktv[2 * j + 1][1]);
       }
     }
     __syncthreads();
-    {
-      const int row = 16 * jt + l16;
-      const int col = 16 * ja + l16;
-      const int rb_h = (jt == 0) ? xR0h : xRh;  // right factors of the row tile's block
-      const int rb_l = (jt == 0) ? xR0l : xRl;
+    if (has_job) {
+      const int row = 16 * jr + l16;
+      const int col = 16 * jc + l16;
+      const int rb_h = (jr == 0) ? xR0h : xRh;  // right factors of the row tile's block
+      const int rb_l = (jr == 0) ? xR0l : xRl;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         const int ea = (row * LDA + 32 * kk + 8 * g4) * 2;
         const int eb = (col * LDA + 32 * kk + 8 * g4) * 2;
         const bf16x8 bh = ld_frag(X, rb_h + eb), bl = ld_frag(X, rb_l + eb);
-#pragma unroll
-        for (int jb = 0; jb < 2; ++jb) {
-          if (jb >= njobs) break;
-          const int mat = (w < 2) ? jb : (w - 2);
-          const bf16x8 ah = ld_frag(X, (mat ? xLQh : xLKh) + ea), al = ld_frag(X, (mat ? xLQl : xLKl) + ea);
-          acc[jb] = mfma(ah, bh, acc[jb]);
-          acc[jb] = mfma(ah, bl, acc[jb]);
-          acc[jb] = mfma(al, bh, acc[jb]);
-        }
+        const bf16x8 ah = ld_frag(X, (mat ? xLQh : xLKh) + ea), al = ld_frag(X, (mat ? xLQl : xLKl) + ea);
+        acc = mfma(ah, bh, acc);
+        acc = mfma(ah, bl, acc);
+        acc = mfma(al, bh, acc);
       }
     }
     __syncthreads();
@@ -446,13 +455,13 @@ __device__ void process_item(const Plan& p, const Item& it, const Inputs& in, ch
     // Below REF = 16 the two diagonal 16 x 16 tiles are built from REF-row sub-blocks and
     // the off-diagonal tile (rows 16..31, columns 0..15) through row 16: for r >= 16 > i,
     // e^{G_r - G_i} = e^{G_r - G_16} e^{G_16 - G_i}, both factors <= 1 whatever the decay.
-    // Jobs: wave 0 (0,0,A) and (1,0,A), wave 1 (0,0,P) and (1,0,P), waves 2 and 3 (1,1,A)
-    // and (1,1,P); acc[0] is the diagonal job, accumulated over the sub-block rounds.
+    // The diagonal jobs (waves 0..3) accumulate over the sub-block rounds; the
+    // off-diagonal jobs (waves 4 and 5) take one round first.
     const float2 g16 = *reinterpret_cast<const float2*>(Gref + (16 / REF) * 128 + c0);
-    if (w < 2) {  // right factors of the off-diagonal tile: rows 0..15, through row 16
+    if (w < kWaves / 2) {  // right factors of the off-diagonal tile: rows 0..15, through row 16
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int r = 8 * w + i;
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * w + i;
         uint32_t h, l;
         split2(kn[i][0] * ex2(g16.x - G[i][0]), kn[i][1] * ex2(g16.y - G[i][1]), h, l);  // <= 1
         const int o = (r * LDA + c0) * 2;
@@ -461,24 +470,24 @@ __device__ void process_item(const Plan& p, const Item& it, const Inputs& in, ch
       }
     }
     __syncthreads();
-    if (w < 2) {
+    if (w == 4 || w == 5) {
       const int row = 16 + l16, col = l16;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         const int ea = (row * LDA + 32 * kk + 8 * g4) * 2;
         const int eb = (col * LDA + 32 * kk + 8 * g4) * 2;
         const bf16x8 bh = ld_frag(X, xRh + eb), bl = ld_frag(X, xRl + eb);
-        const bf16x8 ah = ld_frag(X, (w ? xLQh : xLKh) + ea), al = ld_frag(X, (w ? xLQl : xLKl) + ea);
-        acc[1] = mfma(ah, bh, acc[1]);
-        acc[1] = mfma(ah, bl, acc[1]);
-        acc[1] = mfma(al, bh, acc[1]);
+        const bf16x8 ah = ld_frag(X, (mat ? xLQh : xLKh) + ea), al = ld_frag(X, (mat ? xLQl : xLKl) + ea);
+        acc = mfma(ah, bh, acc);
+        acc = mfma(ah, bl, acc);
+        acc = mfma(al, bh, acc);
       }
     }
     __syncthreads();
-    if (w >= 2) {  // left factors of the lower half with their own sub-block references
+    if (w >= kWaves / 2) {  // left factors of the lower half with their own sub-block references
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int r = 8 * w + i;
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * w + i;
         const float2 gm = *reinterpret_cast<const float2*>(Gref + (r / REF) * 128 + c0);
         const float e0 = ex2(G[i][0] - gm.x), e1 = ex2(G[i][1] - gm.y);  // in [e^-80, 1]
         uint32_t kh, kl, qh, ql;
@@ -492,15 +501,15 @@ __device__ void process_item(const Plan& p, const Item& it, const Inputs& in, ch
       }
     }
     // Round b: sub-block b of both halves at once (rows 16t + b REF .. + REF - 1).
-    const int t = w >= 2 ? 1 : 0;  // this wave's half: its rows and its diagonal tile
+    const int th = w >= kWaves / 2 ? 1 : 0;  // the half this wave's rows are in
     for (int b = 0; b < 16 / REF; ++b) {
-      const int mb = 16 * t + b * REF;
-      const int lim = mb + REF - 1;  // right factors past the sub-block are 0
       {
+        const int mb = 16 * th + b * REF;
+        const int lim = mb + REF - 1;  // right factors past the sub-block are 0
         const float2 gm = *reinterpret_cast<const float2*>(Gref + (mb / REF) * 128 + c0);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int r = 8 * w + i;
+        for (int i = 0; i < 4; ++i) {
+          const int r = 4 * w + i;
           float x0 = 0.f, x1 = 0.f;
           if (r <= lim) {
             x0 = kn[i][0] * ex2(gm.x - G[i][0]);  // <= e^80
@@ -514,11 +523,12 @@ __device__ void process_item(const Plan& p, const Item& it, const Inputs& in, ch
         }
       }
       __syncthreads();
-      {
-        const int row = 16 * t + l16;
+      if (w < 4) {  // the diagonal jobs: tile (jr, jr)
+        const int mb = 16 * jr + b * REF;
+        const int lim = mb + REF - 1;
+        const int row = 16 * jr + l16;
         const bool rowin = (row >= mb) && (row <= lim);
-        const int col = 16 * t + l16;
-        const int mat = w & 1;  // A (waves 0, 2) or P (waves 1, 3)
+        const int col = 16 * jr + l16;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
           const int ea = (row * LDA + 32 * kk + 8 * g4) * 2;
@@ -526,9 +536,9 @@ __device__ void process_item(const Plan& p, const Item& it, const Inputs& in, ch
           const bf16x8 bh = ld_frag(X, xRh + eb), bl = ld_frag(X, xRl + eb);
           bf16x8 ah = ld_frag(X, (mat ? xLQh : xLKh) + ea), al = ld_frag(X, (mat ? xLQl : xLKl) + ea);
           if (!rowin) { ah = bf16x8{}; al = bf16x8{}; }
-          acc[0] = mfma(ah, bh, acc[0]);
-          acc[0] = mfma(ah, bl, acc[0]);
-          acc[0] = mfma(al, bh, acc[0]);
+          acc = mfma(ah, bh, acc);
+          acc = mfma(ah, bl, acc);
+          acc = mfma(al, bh, acc);
         }
       }
       __syncthreads();
@@ -536,47 +546,38 @@ __device__ void process_item(const Plan& p, const Item& it, const Inputs& in, ch
   }
   // Masked, scaled tiles: A strictly lower times beta_r, P lower with diagonal. The tile
   // above the diagonal is written as zeros.
-  {
-    const int col = 16 * ja + l16;
+  if (has_job) {
+    const int col = 16 * jc + l16;
+    float* dst = mat ? Ps : As;
+    const int diag = mat;  // P keeps its diagonal, A does not
 #pragma unroll
-    for (int jb = 0; jb < 2; ++jb) {
-      if (jb >= njobs) break;
-      // REF = 16: waves 0 and 1 hold both matrices of row tile w; below, one matrix of
-      // both row tiles (the layout of the sub-block rounds above).
-      const int mat = (w < 2) ? (REF == 16 ? jb : w) : (w - 2);
-      const int jtj = (w < 2) ? (REF == 16 ? jt : jb) : 1;
-      float* dst = mat ? Ps : As;
-      const int diag = mat;  // P keeps its diagonal, A does not
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = 16 * jtj + 4 * g4 + i;
-        const float sc = mat ? p.scale : betas[row];
-        dst[row * LDF + col] = (col < row + diag) ? sc * acc[jb][i] : 0.f;
-      }
+    for (int i = 0; i < 4; ++i) {
+      const int row = 16 * jr + 4 * g4 + i;
+      const float sc = mat ? p.scale : betas[row];
+      dst[row * LDF + col] = (col < row + diag) ? sc * acc[i] : 0.f;
     }
-    if (w >= 2) {  // upper tile (0,1) of A (wave 2) and of P (wave 3)
-      float* dst = (w == 2) ? As : Ps;
+  } else {  // upper tile (0,1) of A (wave 6) and of P (wave 7)
+    float* dst = (w == 6) ? As : Ps;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dst[(4 * g4 + i) * LDF + 16 + l16] = 0.f;
-    }
+    for (int i = 0; i < 4; ++i) dst[(4 * g4 + i) * LDF + 16 + l16] = 0.f;
   }
 
   // ---------------------------------------------------------------- staging
-  // (the factor tiles are dead after the last barrier of the loop above)
+  // (the factor tiles are dead after the last barrier of the A and P phase)
   {
     const float2 gc = *reinterpret_cast<const float2*>(Gref + NB * 128 + c0);
     // Transposed tiles take rows in pairs: word j of a channel holds rows 2j, 2j + 1.
-    uint32_t v0[4], v1[4];
+    uint32_t v0[2], v1[2];
     if constexpr (REF != 16) {
-      float eg[8][2];
+      float eg[4][2];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < 4; ++i) {
         eg[i][0] = ex2(G[i][0]);  // e^{G_r} <= 1
         eg[i][1] = ex2(G[i][1]);
         qs[i] = cvt_pk(p.scale * qn[i][0] * eg[i][0], p.scale * qn[i][1] * eg[i][1]);
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < 2; ++j) {
         const int i = 2 * j;
         split2(kn[i][0] * eg[i][0], kn[i + 1][0] * eg[i + 1][0], kg0h[j], kg0l[j]);
         split2(kn[i][1] * eg[i][1], kn[i + 1][1] * eg[i + 1][1], kg1h[j], kg1l[j]);
@@ -586,22 +587,20 @@ __device__ void process_item(const Plan& p, const Item& it, const Inputs& in, ch
       }
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) *reinterpret_cast<uint32_t*>(X + xQs + ((8 * w + i) * LDA + c0) * 2) = qs[i];
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint32_t*>(X + xQs + ((4 * w + i) * LDA + c0) * 2) = qs[i];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {  // padding rows of v were loaded as zeros
+    for (int j = 0; j < 2; ++j) {  // padding rows of v were loaded as zeros
       const int i = 2 * j;
       v0[j] = (in.v[i] & 0xffffu) | (in.v[i + 1] << 16);
       v1[j] = (in.v[i] >> 16) | (in.v[i + 1] & 0xffff0000u);
     }
-    st_col8(X, xKGh, c0, w, kg0h);
-    st_col8(X, xKGh, c0 + 1, w, kg1h);
-    st_col8(X, xKGl, c0, w, kg0l);
-    st_col8(X, xKGl, c0 + 1, w, kg1l);
-    st_col8(X, xKt, c0, w, kt0);
-    st_col8(X, xKt, c0 + 1, w, kt1);
-    st_col8(X, xVt, c0, w, v0);
-    st_col8(X, xVt, c0 + 1, w, v1);
-    if (w == 3) *reinterpret_cast<float2*>(rec + kRecE + c0 * 4) = make_float2(ex2(gc.x), ex2(gc.y));
+    st_cols(X, xKGh, lane, w, kg0h, kg1h);
+    st_cols(X, xKGl, lane, w, kg0l, kg1l);
+    st_cols(X, xKt, lane, w, kt0, kt1);
+    st_cols(X, xVt, lane, w, v0, v1);
+    if (w == kWaves - 1) *reinterpret_cast<float2*>(rec + kRecE + c0 * 4) = make_float2(ex2(gc.x), ex2(gc.y));
+    // This item's inputs are dead: the next item's loads overlap the solve and W/U.
+    load_inputs<GF32, GVA>(p, next, w, lane, in);
   }
   __syncthreads();
 
@@ -649,9 +648,9 @@ __device__ void process_item(const Plan& p, const Item& it, const Inputs& in, ch
                                                  t10, 0, 0, 0);
 #pragma unroll
     for (int i = 0; i < 4; ++i) Ts[(16 + 4 * g4 + i) * LDF + l16] = -t10[i];
-  } else {
-    // 18 fragments (Q: 8, K: 8, P: 2), six per wave.
-    for (int f = (w - 1) * 6; f < w * 6; ++f) {
+  } else if (w <= 6) {
+    // 18 fragments (Q: 8, K: 8, P: 2), three per wave on waves 1..6.
+    for (int f = (w - 1) * 3; f < w * 3; ++f) {
       bf16x8 val;
       size_t dst;
       if (f < 8) {
@@ -680,83 +679,84 @@ __device__ void process_item(const Plan& p, const Item& it, const Inputs& in, ch
   __syncthreads();
   // T diag(beta) as hi/lo bf16 (rows r, column r'), zero above the diagonal.
   {
-    // Thread: columns j, j + 1 of row i, twice.
-#pragma unroll
-    for (int q2 = 0; q2 < 2; ++q2) {
-      const int e = tid + 256 * q2;
-      const int i = e >> 4, j = 2 * (e & 15);
-      const float x0 = (j <= i) ? Ts[i * LDF + j] * betas[j] : 0.f;
-      const float x1 = (j + 1 <= i) ? Ts[i * LDF + j + 1] * betas[j + 1] : 0.f;
-      uint32_t hi, lo;
-      split2(x0, x1, hi, lo);
-      *reinterpret_cast<uint32_t*>(X + xTh + (i * LDT + j) * 2) = hi;
-      *reinterpret_cast<uint32_t*>(X + xTl + (i * LDT + j) * 2) = lo;
-    }
+    // Thread: columns j, j + 1 of row i.
+    const int i = tid >> 4, j = 2 * (tid & 15);
+    const float x0 = (j <= i) ? Ts[i * LDF + j] * betas[j] : 0.f;
+    const float x1 = (j + 1 <= i) ? Ts[i * LDF + j + 1] * betas[j + 1] : 0.f;
+    uint32_t hi, lo;
+    split2(x0, x1, hi, lo);
+    *reinterpret_cast<uint32_t*>(X + xTh + (i * LDT + j) * 2) = hi;
+    *reinterpret_cast<uint32_t*>(X + xTl + (i * LDT + j) * 2) = lo;
   }
   __syncthreads();
 
   // ---------------------------------------------------------------- W and U on MFMA
-  // Wave w produces W fragments (t, m = w) and U fragments for value slices 2w, 2w+1.
+  // Wave w produces the W fragment (row tile t = w / 4, key block m = w % 4) and the U
+  // fragment of value tile w.
   {
-    f32x4 dw[2][2], du[2][2];
+    const int t = w >> 2, m = w & 3;
+    bf16x8 th[2], tl[2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int rrow = 16 * t + l16;
-      const bf16x8 th = ld_frag(X, xTh + (rrow * LDT + 8 * g4) * 2);
-      const bf16x8 tl = ld_frag(X, xTl + (rrow * LDT + 8 * g4) * 2);
+    for (int tt = 0; tt < 2; ++tt) {
+      const int rrow = 16 * tt + l16;
+      th[tt] = ld_frag(X, xTh + (rrow * LDT + 8 * g4) * 2);
+      tl[tt] = ld_frag(X, xTl + (rrow * LDT + 8 * g4) * 2);
+    }
+    // Row tile t's fragments read again by address: indexing th/tl with the wave's t
+    // would become a chain of selects.
+    const bf16x8 tht = ld_frag(X, xTh + ((16 * t + l16) * LDT + 8 * g4) * 2);
+    const bf16x8 tlt = ld_frag(X, xTl + ((16 * t + l16) * LDT + 8 * g4) * 2);
+    f32x4 dw[2];
 #pragma unroll
-      for (int q2 = 0; q2 < 2; ++q2) {
-        const int ct = 2 * w + q2;
-        const int crow = 16 * ct + l16;
-        // W^T tile (ct, t) = (k e^G)^T (T diag beta)^T: A = KG^T rows c, B = T' rows r.
-        const bf16x8 kh = ld_frag(X, xKGh + (crow * LDT + 8 * g4) * 2);
-        const bf16x8 kl = ld_frag(X, xKGl + (crow * LDT + 8 * g4) * 2);
-        f32x4 a = zero4();
-        a = mfma(kh, th, a);
-        a = mfma(kh, tl, a);
-        a = mfma(kl, th, a);
-        dw[t][q2] = a;
-        // U tile (t, ct) = T' v: A = T' rows r, B = v columns.
-        const bf16x8 vt = ld_frag(X, xVt + (crow * LDT + 8 * g4) * 2);
+    for (int q2 = 0; q2 < 2; ++q2) {
+      const int crow = 16 * (2 * m + q2) + l16;
+      // W^T tile (key tile 2m + q2, t) = (k e^G)^T (T diag beta)^T: A = KG^T rows c,
+      // B = T' rows r.
+      const bf16x8 kh = ld_frag(X, xKGh + (crow * LDT + 8 * g4) * 2);
+      const bf16x8 kl = ld_frag(X, xKGl + (crow * LDT + 8 * g4) * 2);
+      f32x4 a = zero4();
+      a = mfma(kh, tht, a);
+      a = mfma(kh, tlt, a);
+      a = mfma(kl, tht, a);
+      dw[q2] = a;
+    }
+    // U tile (tt, w) = T' v: A = T' rows r, B = v columns.
+    f32x4 du[2];
+    {
+      const bf16x8 vt = ld_frag(X, xVt + ((16 * w + l16) * LDT + 8 * g4) * 2);
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
         f32x4 uu = zero4();
-        uu = mfma(th, vt, uu);
-        uu = mfma(tl, vt, uu);
-        du[t][q2] = uu;
+        uu = mfma(th[tt], vt, uu);
+        uu = mfma(tl[tt], vt, uu);
+        du[tt] = uu;
       }
     }
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-      *reinterpret_cast<bf16x8*>(rec + kRecW + (size_t)(t * 4 + w) * kFrag + lane * 16) = pack8(-dw[t][0], -dw[t][1]);
-#pragma unroll
-    for (int q2 = 0; q2 < 2; ++q2)
-      *reinterpret_cast<bf16x8*>(rec + kRecU + (size_t)(2 * w + q2) * kFrag + lane * 16) = pack8(du[0][q2], du[1][q2]);
+    *reinterpret_cast<bf16x8*>(rec + kRecW + (size_t)(t * 4 + m) * kFrag + lane * 16) = pack8(-dw[0], -dw[1]);
+    *reinterpret_cast<bf16x8*>(rec + kRecU + (size_t)w * kFrag + lane * 16) = pack8(du[0], du[1]);
   }
 }
 
 template <int REF, bool GF32, bool GVA>
-__global__ __launch_bounds__(kThreadsPrep, 2) void prep_kernel(Plan p, int n_items) {
+__global__ __launch_bounds__(kThreadsPrep, kThreadsPrep / 128) void prep_kernel(Plan p, int n_items) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int step = gridDim.x;
   int item = blockIdx.x;
   if (item >= n_items) return;
-  // Two input buffers; the next item's loads are unconditional (clamped) so the wait
-  // before each item covers only its own inputs.
-  Inputs ia, ib;
-  Item ta = item_of(p, item), tb;
-  load_inputs<GF32, GVA>(p, ta, w, lane, ia);
+  // One input buffer: each item loads the next item's inputs once its own are dead.
+  // Those loads are unconditional (clamped to the last item), so no branch holds them
+  // back and the wait before each item covers only its own inputs.
+  Inputs in;
+  Item cur = item_of(p, item);
+  load_inputs<GF32, GVA>(p, cur, w, lane, in);
   for (;;) {
-    tb = item_of(p, min(item + step, n_items - 1));
-    load_inputs<GF32, GVA>(p, tb, w, lane, ib);
-    process_item<REF>(p, ta, ia, lds, w, lane);
+    const Item nxt = item_of(p, min(item + step, n_items - 1));
+    process_item<REF, GF32, GVA>(p, cur, in, nxt, lds, w, lane);
     item += step;
     if (item >= n_items) break;
-    ta = item_of(p, min(item + step, n_items - 1));
-    load_inputs<GF32, GVA>(p, ta, w, lane, ia);
-    process_item<REF>(p, tb, ib, lds, w, lane);
-    item += step;
-    if (item >= n_items) break;
+    cur = nxt;
   }
 }
 
