@@ -84,12 +84,21 @@ constexpr int xR0h = xRl + kTileA, xR0l = xR0h + kTileA / 2;
 constexpr int xKGh = 0, xKGl = xKGh + kTileT, xKt = xKGl + kTileT, xVt = xKt + kTileT, xQs = xVt + kTileT,
               xTh = xQs + kTileA, xTl = xTh + kTileTT;
 
-// Inputs of one item held by one thread: rows 4w .. 4w+3, channels 2l, 2l+1.
+// Inputs of one item held by one thread: rows 4w .. 4w+3, channels 2l, 2l+1. The words
+// are kept as loaded and widened where they are used: arithmetic on a loaded value makes
+// the compiler wait for that load (and for every load issued before it) right there.
 struct Inputs {
   uint32_t q[4], k[4], v[4];  // two bf16 each
-  float2 g[4];                // raw gate (fp32, or bf16 widened on load)
-  float braw;                 // raw beta of row 4w + (lane & 3) (lanes 0..3 meaningful)
+  uint32_t g[4][2];           // raw gate: two fp32, or two bf16 in word 0
+  uint32_t bhi, blo;          // raw beta of row 4w + (lane & 3) (lanes 0..3 meaningful):
+                              // upper and lower 16 bits of an fp32 value, or the bf16 twice
 };
+
+template <bool GF32>
+__device__ __forceinline__ float2 gate_of(const uint32_t* g) {
+  if constexpr (GF32) return make_float2(__uint_as_float(g[0]), __uint_as_float(g[1]));
+  return make_float2(__uint_as_float(g[0] << 16), __uint_as_float(g[0] & 0xffff0000u));
+}
 
 struct Item {
   int cid, h, seq, t0, len;
@@ -141,10 +150,10 @@ __device__ __forceinline__ void load_inputs(const Plan& p, const Item& it, int w
       in.v[i] = __builtin_amdgcn_raw_buffer_load_b32(rv, vo, 0, kPolicy);
       if constexpr (GF32) {
         const auto g = __builtin_amdgcn_raw_buffer_load_b64(rg, 2 * vo, 0, kPolicy);
-        in.g[i] = make_float2(__uint_as_float(g[0]), __uint_as_float(g[1]));
+        in.g[i][0] = g[0];
+        in.g[i][1] = g[1];
       } else {
-        const uint32_t g = __builtin_amdgcn_raw_buffer_load_b32(rg, vo, 0, kPolicy);
-        in.g[i] = make_float2(__uint_as_float(g << 16), __uint_as_float(g & 0xffff0000u));
+        in.g[i][0] = __builtin_amdgcn_raw_buffer_load_b32(rg, vo, 0, kPolicy);
       }
     }
   };
@@ -157,9 +166,8 @@ __device__ __forceinline__ void load_inputs(const Plan& p, const Item& it, int w
   const size_t bidx = (size_t)brow * H + it.h;
   const bool bf = p.beta_dtype != kF32;
   const char* bb = reinterpret_cast<const char*>(p.beta_raw);
-  const uint32_t bhi = *reinterpret_cast<const uint16_t*>(bb + (bf ? bidx * 2 : bidx * 4 + 2));
-  const uint32_t blo = *reinterpret_cast<const uint16_t*>(bb + (bf ? bidx * 2 : bidx * 4));
-  in.braw = __uint_as_float((bhi << 16) | (bf ? 0u : blo));
+  in.bhi = *reinterpret_cast<const uint16_t*>(bb + (bf ? bidx * 2 : bidx * 4 + 2));
+  in.blo = *reinterpret_cast<const uint16_t*>(bb + (bf ? bidx * 2 : bidx * 4));
 }
 
 __device__ __forceinline__ float lo16(uint32_t x) { return __uint_as_float(x << 16); }
@@ -310,13 +318,15 @@ __device__ void process_item(const Plan& p, const Item& it, Inputs& in, const It
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const bool valid = 4 * w + i < len;
-      run0 += valid ? lb2 * sigm(in.g[i].x) : 0.f;
-      run1 += valid ? lb2 * sigm(in.g[i].y) : 0.f;
+      const float2 g = gate_of<GF32>(in.g[i]);
+      run0 += valid ? lb2 * sigm(g.x) : 0.f;
+      run1 += valid ? lb2 * sigm(g.y) : 0.f;
       G[i][0] = run0;
       G[i][1] = run1;
     }
     *reinterpret_cast<float2*>(tot + w * 128 + c0) = make_float2(run0, run1);
-    if (lane < 4) betas[4 * w + lane] = (4 * w + lane < len) ? sigm(in.braw) : 0.f;
+    const float braw = __uint_as_float((in.bhi << 16) | (p.beta_dtype != kF32 ? 0u : in.blo));
+    if (lane < 4) betas[4 * w + lane] = (4 * w + lane < len) ? sigm(braw) : 0.f;
   }
   __syncthreads();
   {
