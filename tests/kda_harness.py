@@ -16,6 +16,7 @@ OUT_TOL = 5e-3          # output rel-L2 vs the fp64 oracle
 STATE_TOL_F32 = 5e-3    # final state rel-L2 with fp32 state storage
 STATE_TOL_2B = 1e-2     # final state rel-L2 with fp16 / bf16 state storage
 ROW_TOL = 2.5e-2        # one output row (token, head), relative to max(|row|, RMS row of its (seq, head))
+SEQ_BAR_ROWS = 32       # (sequence, head)s with fewer rows take twice the output bar (see compare)
 
 
 def rel_l2(x, ref) -> float:
@@ -132,7 +133,11 @@ def compare(wl: Workload, run: GpuRun, seqs=None, heads=None, out_tol=OUT_TOL, s
             row_tol=ROW_TOL):
     """GPU output and final states against the oracle, bounded per (sequence, head).
 
-    - output rel-L2 of every (sequence, head) over its valid rows <= out_tol;
+    - output rel-L2 of the whole call <= out_tol;
+    - output rel-L2 of every (sequence, head) with at least SEQ_BAR_ROWS valid rows <=
+      out_tol, and <= 2 * out_tol below that: over a handful of rows the rel-L2 is a
+      row-level figure (for a one-token sequence it is one bf16 row, and single rows of
+      long sequences reach 6-8e-3 on the chunked path);
     - every output row (one token, one head) within row_tol of the oracle, relative to
       the larger of its own norm and the RMS row norm of its (sequence, head), so that a
       single wrong row cannot hide in a long sequence;
@@ -147,6 +152,7 @@ def compare(wl: Workload, run: GpuRun, seqs=None, heads=None, out_tol=OUT_TOL, s
     if state_tol is None:
         state_tol = STATE_TOL_F32 if wl.state_dtype == "f32" else STATE_TOL_2B
     worst_out, worst_row, worst_state = (0.0, None), (0.0, None), (0.0, None)
+    worst_short = (0.0, None)  # (sequence, head)s with fewer than SEQ_BAR_ROWS rows
     num = den = 0.0
     for n in seq_ids:
         a, b = int(cu[n]), int(cu[n + 1])
@@ -160,8 +166,11 @@ def compare(wl: Workload, run: GpuRun, seqs=None, heads=None, out_tol=OUT_TOL, s
             num += float(np.sum(d * d))
             den += float(np.sum(ref * ref))
             e = rel_l2(got, ref)
-            if e > worst_out[0] or worst_out[1] is None:
-                worst_out = (e, (n, h))
+            if b - a >= SEQ_BAR_ROWS:
+                if e > worst_out[0] or worst_out[1] is None:
+                    worst_out = (e, (n, h))
+            elif e > worst_short[0] or worst_short[1] is None:
+                worst_short = (e, (n, h))
             rn = np.linalg.norm(ref, axis=1)
             floor = max(float(np.sqrt(np.mean(rn * rn))), 1e-30)
             rr = np.linalg.norm(d, axis=1) / np.maximum(rn, floor)
@@ -184,16 +193,21 @@ def compare(wl: Workload, run: GpuRun, seqs=None, heads=None, out_tol=OUT_TOL, s
     glob_out = float(np.sqrt(num / den)) if den > 0 else 0.0
     glob_state = float(np.sqrt(snum / sden)) if sden > 0 else 0.0
     print(f"  {wl.name}: {len(seq_ids)} seq x {len(hs)} heads; output rel-L2 worst {worst_out[0]:.3e} "
-          f"at (seq, head) {worst_out[1]}, whole {glob_out:.3e}; worst row {worst_row[0]:.3e} at "
+          f"at (seq, head) {worst_out[1]}"
+          + (f" (shorter than a chunk: {worst_short[0]:.3e} at {worst_short[1]})" if worst_short[1] else "")
+          + f", whole {glob_out:.3e}; worst row {worst_row[0]:.3e} at "
           f"(seq, head, token) {worst_row[1]}"
           + (f"; state rel-L2 worst {worst_state[0]:.3e} at {worst_state[1]}, whole {glob_state:.3e}"
              if fins is not None else ""), flush=True)
+    assert glob_out <= out_tol, f"{wl.name}: whole-call output rel-L2 {glob_out:.3e} > {out_tol}"
     assert worst_out[0] <= out_tol, f"{wl.name}: output rel-L2 {worst_out[0]:.3e} > {out_tol} at {worst_out[1]}"
+    assert worst_short[0] <= 2 * out_tol, \
+        f"{wl.name}: output rel-L2 {worst_short[0]:.3e} > {2 * out_tol} at {worst_short[1]} (fewer than a chunk of rows)"
     assert worst_row[0] <= row_tol, f"{wl.name}: output row error {worst_row[0]:.3e} > {row_tol} at {worst_row[1]}"
     if fins is not None:
         assert worst_state[0] <= state_tol, \
             f"{wl.name}: state rel-L2 {worst_state[0]:.3e} > {state_tol} at {worst_state[1]}"
-    return worst_out[0], (worst_state[0] if fins is not None else None)
+    return max(worst_out[0], worst_short[0]), (worst_state[0] if fins is not None else None)
 
 
 def untouched_slots_bitwise(wl: Workload, run: GpuRun):

@@ -20,7 +20,7 @@ from tests.kda_harness import compare, run_gpu, untouched_slots_bitwise
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 48
+N_CASES = 96
 
 
 def _draw(case: int) -> dict:
@@ -92,7 +92,7 @@ def _context(**env):
     return _CONTEXTS[key]
 
 
-@pytest.mark.parametrize("case", range(16))
+@pytest.mark.parametrize("case", range(32))
 def test_random_call_forced_kernels_matches_oracle(case):
     kw = _draw(100 + case)
     env = {"KDA_DV_SPLIT": (1, 2, 4, 8)[case % 4]}
