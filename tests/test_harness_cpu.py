@@ -32,3 +32,36 @@ def test_pooled_oracle_equals_direct_call(workers, mode):
     assert np.all(np.isnan(np.delete(out, rows, axis=0)))
     for n in seqs:
         assert np.array_equal(fin[n], ref_fin[n][heads])
+
+
+def _planted(wl, ref, seq, eps, row=None):
+    """The oracle's output with sequence seq (or one row of it) scaled by 1 + eps."""
+    got = np.array(ref, copy=True)
+    cu = wl.cu_seqlens.numpy()
+    a, b = int(cu[seq]), int(cu[seq + 1])
+    if row is None:
+        got[a:b] *= 1.0 + eps
+    else:
+        got[a + row] *= 1.0 + eps
+    return got
+
+
+def test_compare_bars_catch_what_they_should():
+    """compare() on planted errors, each sized to trip one bar and no other: a (sequence,
+    head) of at least one chunk is held to 5e-3, one shorter than a chunk to twice that,
+    every row to the row bar (2.5e-2), and the whole call to 5e-3."""
+    from tests.kda_harness import GpuRun, compare
+    wl = make_workload("bars", [1, 40, 300], H=2, seed=9, state_mode="none")
+    ref, _ = run_oracle(wl, workers=0)
+    ok = lambda got: compare(wl, GpuRun(got, None, None))
+    ok(ref)
+    ok(_planted(wl, ref, 0, 6e-3))                    # one-token sequence: within twice the bar
+    ok(_planted(wl, ref, 2, 2e-2, row=100))           # one row under the row bar
+    with pytest.raises(AssertionError, match=r"output rel-L2 .* at \(1, "):
+        ok(_planted(wl, ref, 1, 6e-3))                # 40 rows over the bar, the call within it
+    with pytest.raises(AssertionError, match="fewer than a chunk"):
+        ok(_planted(wl, ref, 0, 1.2e-2))              # one-token sequence over twice the bar
+    with pytest.raises(AssertionError, match="row error"):
+        ok(_planted(wl, ref, 2, 3e-2, row=100))       # one row over the row bar, its sequence within
+    with pytest.raises(AssertionError, match="whole-call"):
+        ok(ref * (1.0 + 6e-3))                        # everything 6e-3 off
