@@ -639,11 +639,16 @@ __global__ __launch_bounds__(256, 1) void scan_narrow(Plan p, int units, int gro
           Db[nt] = pack8(x[nt][0], x[nt][1]);
           *reinterpret_cast<bf16x8*>(lds + L::db(par, nt) + vo) = Db[nt];
         }
+        // Every LDS write of the step is issued before the update MFMAs, and the barrier
+        // after them (below), so that the MFMAs cover the writes' latency; sunk below the
+        // MFMAs, or the barrier hoisted above them, the writes would hold its wait.
+        __builtin_amdgcn_sched_barrier(0);
         // S^T = Diag(E) S^T + K^T Delta.
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
           for (int tt = 0; tt < 8; ++tt) S[nt][tt] = mfma(f.k[tt], Db[nt], S[nt][tt]);
+        __builtin_amdgcn_sched_barrier(0);
         barrier_lds();  // publishes Sb, Db; the loader has chunk c + 1 in the next slot
         slot = (slot + 1 == RING) ? 0 : slot + 1;
         if (c + 1 < nc) read(f, slot);
