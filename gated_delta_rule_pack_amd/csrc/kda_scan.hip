@@ -102,6 +102,40 @@ __device__ __forceinline__ void decay_state(f32x4 (&S)[8], const float (&e)[2]) 
   }
 }
 
+// S^T[k][v] *= exp(G_C)[k] for key tile TT alone.
+template <int TT>
+__device__ __forceinline__ void decay_tile(f32x4& s, const float (&e)[2]) {
+  constexpr int J = 4 * (TT & 3);
+  s[0] *= row_bcast<J + 0>(e[TT >> 2]);
+  s[1] *= row_bcast<J + 1>(e[TT >> 2]);
+  s[2] *= row_bcast<J + 2>(e[TT >> 2]);
+  s[3] *= row_bcast<J + 3>(e[TT >> 2]);
+}
+
+// S^T = Diag(E) S^T + K^T Delta, key tile by key tile, for a state whose tiles 0 and 1
+// are already decayed: the decay of tile TT + 2 is issued next to the update MFMA of
+// tile TT, so that its multiplies run while the matrix unit works (the schedule is fixed
+// by the group barriers in update_groups).
+template <int TT = 0>
+__device__ __forceinline__ void update_interleaved(f32x4 (&S)[8], const bf16x8 (&k)[8], bf16x8 db, const float (&e)[2]) {
+  if constexpr (TT < 8) {
+    S[TT] = mfma(k[TT], db, S[TT]);
+    if constexpr (TT + 2 < 8) decay_tile<TT + 2>(S[TT + 2], e);
+    update_interleaved<TT + 1>(S, k, db, e);
+  }
+}
+
+// Issue order of one update_interleaved: each update MFMA, then the four multiplies of
+// a later tile's decay.
+template <int TT = 0>
+__device__ __forceinline__ void update_groups() {
+  if constexpr (TT < 8) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // one MFMA
+    if constexpr (TT + 2 < 8) __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // four VALU
+    update_groups<TT + 1>();
+  }
+}
+
 // A operand that copies U into the Delta accumulators on the matrix unit instead of
 // widening it on the vector ALU. The U fragment, taken as a B operand, holds in element
 // j of lane group g the chunk row 16*(j/4) + 4g + j%4 (the accumulator rows of both row
@@ -630,9 +664,13 @@ __global__ __launch_bounds__(256, 1) void scan_narrow(Plan p, int units, int gro
         for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
           for (int m = 0; m < 4; ++m) *reinterpret_cast<bf16x8*>(lds + L::sb(par, nt, m) + vo) = Sb[nt][m];
-        // Diag(E) S^T while the MFMAs above run.
+        // Diag(E) S^T for key tiles 0 and 1 while the last Delta MFMAs run; the other
+        // tiles' decay goes between the update MFMAs below.
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) decay_state(S[nt], f.e);
+        for (int nt = 0; nt < NT; ++nt) {
+          decay_tile<0>(S[nt][0], f.e);
+          decay_tile<1>(S[nt][1], f.e);
+        }
         bf16x8 Db[NT];
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
@@ -645,9 +683,9 @@ __global__ __launch_bounds__(256, 1) void scan_narrow(Plan p, int units, int gro
         __builtin_amdgcn_sched_barrier(0);
         // S^T = Diag(E) S^T + K^T Delta.
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
+        for (int nt = 0; nt < NT; ++nt) update_interleaved(S[nt], f.k, Db[nt], f.e);
 #pragma unroll
-          for (int tt = 0; tt < 8; ++tt) S[nt][tt] = mfma(f.k[tt], Db[nt], S[nt][tt]);
+        for (int nt = 0; nt < NT; ++nt) update_groups();
         __builtin_amdgcn_sched_barrier(0);
         barrier_lds();  // publishes Sb, Db; the loader has chunk c + 1 in the next slot
         slot = (slot + 1 == RING) ? 0 : slot + 1;
