@@ -89,18 +89,6 @@ __device__ __forceinline__ float row_bcast(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x150 + J, 0xf, 0xf, true));
 }
 
-// S^T[k][v] *= exp(G_C)[k] for key tiles TT..7.
-template <int TT = 0>
-__device__ __forceinline__ void decay_state(f32x4 (&S)[8], const float (&e)[2]) {
-  if constexpr (TT < 8) {
-    constexpr int J = 4 * (TT & 3);
-    S[TT][0] *= row_bcast<J + 0>(e[TT >> 2]);
-    S[TT][1] *= row_bcast<J + 1>(e[TT >> 2]);
-    S[TT][2] *= row_bcast<J + 2>(e[TT >> 2]);
-    S[TT][3] *= row_bcast<J + 3>(e[TT >> 2]);
-    decay_state<TT + 1>(S, e);
-  }
-}
 
 // S^T[k][v] *= exp(G_C)[k] for key tile TT alone.
 template <int TT>
@@ -110,6 +98,15 @@ __device__ __forceinline__ void decay_tile(f32x4& s, const float (&e)[2]) {
   s[1] *= row_bcast<J + 1>(e[TT >> 2]);
   s[2] *= row_bcast<J + 2>(e[TT >> 2]);
   s[3] *= row_bcast<J + 3>(e[TT >> 2]);
+}
+
+// S^T[k][v] *= exp(G_C)[k] for key tiles TT..7.
+template <int TT = 0>
+__device__ __forceinline__ void decay_state(f32x4 (&S)[8], const float (&e)[2]) {
+  if constexpr (TT < 8) {
+    decay_tile<TT>(S[TT], e);
+    decay_state<TT + 1>(S, e);
+  }
 }
 
 // S^T = Diag(E) S^T + K^T Delta, key tile by key tile, for a state whose tiles 0 and 1
