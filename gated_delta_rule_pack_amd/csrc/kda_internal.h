@@ -10,7 +10,6 @@ namespace kda {
 constexpr int kChunk = 32;    // tokens per chunk
 constexpr int kHead = 128;    // K = V = 128
 constexpr int kThreadsPrep = 512;
-constexpr int kThreadsScan = 256;
 
 // Per (head, chunk) workspace record written by prep and read by scan. Every tile is
 // stored in the exact per-lane order the scan's MFMA operands use, so the scan issues

@@ -499,8 +499,9 @@ __device__ __forceinline__ void pipelined_chunks(int nc, LoadF&& load, StepF&& s
 // ====================================================================== narrow slices
 // For few (segment, head) units, where per-chunk latency rather than the chip's total
 // load bandwidth bounds the call: 16*NT value channels per workgroup, one state wave,
-// two output waves and a loader, so that the state wave's chain carries no output work
-// and reads only W, K, U and E.
+// one output wave (both row tiles, so the published state copy and Delta are read once
+// per chunk) and a loader, so that the state wave's chain carries no output work and
+// reads only W, K, U and E.
 // LDS: a ring of RING slots with the state wave's fragments of one chunk each (W 8, K 8,
 // U NT fragments of 1 KB, E 128 fp32), then, per chunk parity, the published bf16 state
 // copy Sb [NT][4 key blocks] and Delta Db [NT] as 1 KB operand rows.
@@ -519,7 +520,7 @@ struct NarrowLds {
 };
 
 template <int NT, int SDT, int RING, int DOUT, bool KF>
-__global__ __launch_bounds__(256, 1) void scan_narrow(Plan p, int units, int groups) {
+__global__ __launch_bounds__(192, 1) void scan_narrow(Plan p, int units, int groups) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   typedef NarrowLds<NT, RING> L;
   Unit un;
@@ -537,7 +538,7 @@ __global__ __launch_bounds__(256, 1) void scan_narrow(Plan p, int units, int gro
       __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(rec0), (short)0, nc * (int)kRecBytes, kBufWord3);
   const int vo = lane * 16;  // lane offset inside a fragment
 
-  if (wave == 3) {
+  if (wave == 2) {
     // ------------------------------------------------------------ loader wave
     // Chunk c goes to slot c mod RING, RING - 1 chunks ahead. Before barrier c (and
     // before the first barrier, for chunk 0) it waits until chunk c + 1 has landed.
@@ -699,17 +700,22 @@ __global__ __launch_bounds__(256, 1) void scan_narrow(Plan p, int units, int gro
           store_state4_vk<SDT>(out_plane, 16 * (vtile0 + nt) + l16, 16 * tt + 4 * g4, S[nt][tt], KF);
     }
   } else {
-    // ------------------------------------------------------------ output waves
-    const int t = wave - 1;  // row tile
+    // ------------------------------------------------------------ output wave
+    // Both row tiles, so that the published Sb and Db are read from LDS once per chunk.
     const size_t row_stride = (size_t)p.H * kHead;
     // Lane holds O^T rows v = 16*(vtile0+nt) + 4*g4 .. +3 of token row 16*t + l16.
-    const int orow = 16 * t + l16;
-    const size_t ooff = (size_t)orow * row_stride + (size_t)h * kHead + 16 * vtile0 + 4 * g4;
-    typedef OutFrags F;
+    const size_t ooff = (size_t)l16 * row_stride + (size_t)h * kHead + 16 * vtile0 + 4 * g4;
+    struct F {
+      OutFrags t[2];
+    };
     if (nc > 0) {
       barrier_lds();  // pairs with the first barrier of the other waves
       pipelined_chunks<DOUT, F>(
-          nc, [&](F& f, int c) { load_out_frags(f, rs, c * (int)kRecBytes, vo, t); },
+          nc,
+          [&](F& f, int c) {
+            load_out_frags(f.t[0], rs, c * (int)kRecBytes, vo, 0);
+            load_out_frags(f.t[1], rs, c * (int)kRecBytes, vo, 1);
+          },
           [&](const F& f, int c) {
             const int par = c & 1;
             barrier_lds();  // the state wave has published chunk c's Sb and Db
@@ -718,15 +724,21 @@ __global__ __launch_bounds__(256, 1) void scan_narrow(Plan p, int units, int gro
             __bf16* out_c = reinterpret_cast<__bf16*>(p.out) + (size_t)t0 * row_stride + ooff;
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
-              // (Q S^T)^T = S Q^T, then + Delta^T P^T.
-              f32x4 o = zero4();
+              bf16x8 sb[4];
 #pragma unroll
-              for (int m = 0; m < 4; ++m)
-                o = mfma(*reinterpret_cast<const bf16x8*>(lds + L::sb(par, nt, m) + vo), f.q[m], o);
-              o = mfma(*reinterpret_cast<const bf16x8*>(lds + L::db(par, nt) + vo), f.p, o);
-              if (orow < len) {
-                const bf16x4 ov = {to_bf16(o[0]), to_bf16(o[1]), to_bf16(o[2]), to_bf16(o[3])};
-                *reinterpret_cast<bf16x4*>(out_c + 16 * nt) = ov;
+              for (int m = 0; m < 4; ++m) sb[m] = *reinterpret_cast<const bf16x8*>(lds + L::sb(par, nt, m) + vo);
+              const bf16x8 db = *reinterpret_cast<const bf16x8*>(lds + L::db(par, nt) + vo);
+#pragma unroll
+              for (int t = 0; t < 2; ++t) {
+                // (Q S^T)^T = S Q^T, then + Delta^T P^T.
+                f32x4 o = zero4();
+#pragma unroll
+                for (int m = 0; m < 4; ++m) o = mfma(sb[m], f.t[t].q[m], o);
+                o = mfma(db, f.t[t].p, o);
+                if (16 * t + l16 < len) {
+                  const bf16x4 ov = {to_bf16(o[0]), to_bf16(o[1]), to_bf16(o[2]), to_bf16(o[3])};
+                  *reinterpret_cast<bf16x4*>(out_c + (size_t)16 * t * row_stride + 16 * nt) = ov;
+                }
               }
             }
           });
@@ -770,7 +782,7 @@ int launch_narrow(const Plan& p, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   const int groups = 8 / NT;
   const int units = p.n_seg * p.H;
   const int nblocks = 8 * ((units + 7) / 8) * groups;
-  hipExtLaunchKernelGGL((scan_narrow<NT, SDT, R, DO, KF>), dim3(nblocks), dim3(256), bytes, s, e0, e1, 0, p, units, groups);
+  hipExtLaunchKernelGGL((scan_narrow<NT, SDT, R, DO, KF>), dim3(nblocks), dim3(192), bytes, s, e0, e1, 0, p, units, groups);
   return (int)hipGetLastError();
 }
 
